@@ -1,0 +1,140 @@
+/*
+ * libpisa - PISA piecewise sparse attention, forward pass, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (per batch-head; the pages describing "PISA: Piecewise Sparse Attention Is Wiser
+ * for Efficient Diffusion Transformers"):
+ *   - Q, K, V are cut into blocks of B rows (AI Radio episode, paper summary; gist.science
+ *     technical summary, section 2 "Core algorithm"). Query block i keeps a critical set S_i of k
+ *     key/value blocks, computed exactly; the other blocks U_i are approximated.
+ *   - Precompute (gist.science section 2 "Hardware implementation"): per block the key centroid
+ *     kbar_j, the value sum, the block first-order matrix H_j = sum_n (k_n - kbar_j)^T v_n, their
+ *     mean H-bar over all blocks, and M_j = ||H_j - H-bar||_F for routing (section 2
+ *     "Covariance-aware routing").
+ *   - Routing: S_i = the k largest Score_{i,j} = qbar_i . kbar_j + ln(n_j + ||qbar_i|| M_j)
+ *     (qbar_i = mean scaled query of block i; ties to the lower j). The pages name the score's
+ *     ingredients but print no formula: this is the library's reading (PISA_ROUTING_PLAIN drops
+ *     the covariance term).
+ *   - Output (gist.science section 2 "Core algorithm", numerator formula): o_t = N_t / D_t with
+ *       N_t = sum_{j in S_i} sum_n e^{q~_t.k_n} v_n + sum_{j in U_i} alpha_{t,j} sum_n v_{j,n}
+ *             + beta_t (q~_t H-bar),       alpha_{t,j} = e^{q~_t.kbar_j},  beta_t = sum_U alpha
+ *       D_t = sum_{j in S_i} sum_n e^{q~_t.k_n} + sum_{j in U_i} n_j alpha_{t,j}
+ *     q~ = scale * q (default scale 1/sqrt(d)). D_t has no first-order part because kbar_j is
+ *     the block mean.
+ *
+ * Layout: Q, K, V and out are contiguous [H, L, d] (batch folded into H: every statistic is per
+ * batch-head), row-major, all of one dtype (bf16 or fp32), 16-byte aligned device pointers. out
+ * must not overlap Q, K or V. A ragged last block (L % B != 0) is handled.
+ *
+ * Ownership: the caller owns Q, K, V, out and the workspace (device memory attached with
+ * pisa_plan_attach_workspace); the plan owns host state only. pisa_plan/_set/_info/_destroy make
+ * no HIP call. pisa_forward* enqueue kernels on `stream` and return without synchronising; a plan
+ * (its workspace) must not be used by two calls that can run concurrently.
+ *
+ * Errors: every call returns a pisa_status and never aborts. Argument errors are reported before
+ * any launch; a failed launch or missing device returns PISA_ERR_DEVICE. pisa_last_error() gives
+ * the calling thread's last error text.
+ *
+ * Supported: dtype bf16 with d = 128, B in {64, 128}; dtype fp32 with d in {64, 128},
+ * B in {64, 128}; L >= 1, H >= 1, 0 < keep <= 1, H * L * d < 2^31 elements per tensor.
+ */
+#ifndef PISA_H_
+#define PISA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct pisa_plan_s pisa_plan_t;
+
+typedef enum pisa_status {
+  PISA_OK = 0,
+  PISA_ERR_INVALID_ARGUMENT = 1, /* bad size, option value or pointer */
+  PISA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (d, B, dtype combination) */
+  PISA_ERR_INVALID_HANDLE = 3,   /* NULL or destroyed plan */
+  PISA_ERR_WORKSPACE = 4,        /* no workspace attached, too small or misaligned */
+  PISA_ERR_DEVICE = 5            /* no HIP device, or a HIP call / kernel launch failed */
+} pisa_status;
+
+typedef enum pisa_option {
+  PISA_OPT_DTYPE = 0,   /* PISA_DTYPE_BF16 (default for d = 128) or PISA_DTYPE_F32 (default otherwise) */
+  PISA_OPT_SCALE = 1,   /* softmax scale tau > 0 applied to q (default 1/sqrt(d)) */
+  PISA_OPT_ROUTING = 2, /* PISA_ROUTING_COV (default) or PISA_ROUTING_PLAIN */
+  PISA_OPT_PHASES = 3   /* bit mask of PISA_PHASE_* (default all three); EXACT must be set */
+} pisa_option;
+
+enum { PISA_DTYPE_BF16 = 0, PISA_DTYPE_F32 = 1 };
+enum { PISA_ROUTING_COV = 0, PISA_ROUTING_PLAIN = 1 };
+/* PHASES = EXACT alone is keep-or-drop block-sparse attention; EXACT|ZEROTH omits H-bar. */
+enum { PISA_PHASE_EXACT = 1, PISA_PHASE_ZEROTH = 2, PISA_PHASE_FIRST = 4 };
+
+typedef struct pisa_plan_info {
+  int64_t L;
+  int32_t H, d, B;
+  int32_t n_blocks;     /* N_b = ceil(L / B) */
+  int32_t k;            /* critical blocks per query block: clamp(ceil(keep N_b - 1e-9), 1, N_b) */
+  int32_t n_last;       /* rows of the last block */
+  int32_t dtype, routing, phases;
+  double scale;
+  size_t workspace_bytes;   /* device bytes pisa_plan_attach_workspace needs (256-B aligned) */
+  double flops_stats;       /* 2 * 2 L d^2 per head: K^T V for H-bar and again for M_j */
+  double flops_route;       /* 2 N_b^2 d per head */
+  double flops_first;       /* 2 L d^2 per head (q H-bar) */
+  double bytes_stats;       /* compulsory HBM bytes of the statistics kernels (reads Q,K,V,K,V) */
+} pisa_plan_info_t;
+
+/* Create a plan for H heads of L tokens, head dim d, block size B, keeping a fraction `keep` of
+ * the N_b key/value blocks per query block. Host only. */
+pisa_status pisa_plan(int64_t L, int32_t H, int32_t d, int32_t B, double keep, pisa_plan_t **plan);
+
+/* Set an option (see pisa_option). Changing the dtype changes workspace_bytes: re-attach. */
+pisa_status pisa_plan_set(pisa_plan_t *plan, pisa_option opt, double value);
+
+/* Sizes, derived counts and the FLOP/byte model of the plan. */
+pisa_status pisa_plan_info(const pisa_plan_t *plan, pisa_plan_info_t *info);
+
+/* Attach caller-owned device memory of at least info.workspace_bytes, 256-byte aligned. The
+ * plan keeps the pointer, not ownership. */
+pisa_status pisa_plan_attach_workspace(pisa_plan_t *plan, void *dev_ptr, size_t bytes);
+
+/* The whole forward pass: statistics, routing, fused piecewise attention. Enqueued on `stream`
+ * (asynchronous). Equivalent to pisa_forward_stats + pisa_forward_route + pisa_forward_attend. */
+pisa_status pisa_forward(pisa_plan_t *plan, const void *Q, const void *K, const void *V, void *out,
+                         hipStream_t stream);
+
+/* Stage 1: block statistics into the workspace (centroids, value sums, pooled queries, H-bar,
+ * M_j). Reads Q, K, V. */
+pisa_status pisa_forward_stats(pisa_plan_t *plan, const void *Q, const void *K, const void *V,
+                               hipStream_t stream);
+
+/* Stage 2: routing scores and per-query-block top-k into the workspace (needs stage 1). */
+pisa_status pisa_forward_route(pisa_plan_t *plan, hipStream_t stream);
+
+/* Stage 3: fused piecewise attention (needs stages 1 and 2 on the same inputs). */
+pisa_status pisa_forward_attend(pisa_plan_t *plan, const void *Q, const void *K, const void *V,
+                                void *out, hipStream_t stream);
+
+/* Destroy a plan (does not free the attached workspace). Destroying NULL or twice returns
+ * PISA_ERR_INVALID_HANDLE. */
+pisa_status pisa_plan_destroy(pisa_plan_t *plan);
+
+const char *pisa_status_string(pisa_status s);
+const char *pisa_last_error(void);
+
+/* Test support: copy statistics out of the workspace after a forward (async on `stream`, any
+ * memory the HIP runtime can address; a NULL destination is skipped). Shapes (fp32):
+ * qbar, kbar, vsum [H, N_b, d]; hbar [H, d, d]; M [H, N_b]. */
+pisa_status pisa_debug_copy_stats(pisa_plan_t *plan, float *qbar, float *kbar, float *vsum,
+                                  float *hbar, float *M, hipStream_t stream);
+
+/* Test support: copy the selection: idx [H, N_b, k] int32, ascending block indices per row. */
+pisa_status pisa_debug_copy_selection(pisa_plan_t *plan, int32_t *idx, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PISA_H_ */

@@ -1,0 +1,116 @@
+// Device-side building blocks for the gfx950 kernels of libpisa: vector types, MFMA wrappers,
+// buffer-resource loads (out-of-range bytes read as zero), direct global->LDS copies, the LDS
+// transpose read, and the LDS tile swizzles.
+//
+// Lane layouts used throughout (checked on gfx950 with an in-bounds probe):
+//   v_mfma_f32_32x32x16_bf16: A[i][k] -> lane i + 32*(k/8), element k%8; B[k][j] -> lane
+//   j + 32*(k/8), element k%8; D[i][j] -> lane j + 32*((i/4)%2), accumulator (i%4) + 4*(i/8).
+//   ds_read_b64_tr_b16: within each 16-lane group, lane r supplies the address of 4 consecutive
+//   16-bit values M[r][0..3]; lane i receives {M[4e + i/4][i%4] : e = 0..3}.
+//   Direct global->LDS 16-byte loads write lane l's data at (wave-uniform base) + 16*l.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pisa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+
+// 16-byte global load through a buffer resource: bytes past the resource's range read as 0.
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+}
+
+// Direct copy global -> LDS of 16 bytes per lane: lane l's bytes land at lds_base + 16*l
+// (lds_base must be wave-uniform). Bytes past the resource's range are written as 0.
+__device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, 0, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ i16x4 lds_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+}
+
+__device__ __forceinline__ bf16x8 join_tr(i16x4 a, i16x4 b) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS tiles of R rows x 128 bf16 (256 bytes = 16 chunks of 16 bytes per row).
+// "row-read" tiles are read 16 bytes per lane along a row by 32 consecutive rows (MFMA operand
+// whose contiguous dimension is the reduction): chunk c of row r is stored at c ^ (r & 15).
+// "transpose-read" tiles are read with ds_read_b64_tr_b16 over 4 consecutive rows x 32 bytes
+// per 16-lane group: chunk c of row r is stored at c ^ ((r & 3) << 2).
+__device__ __forceinline__ uint32_t swz_row(uint32_t r, uint32_t c) { return c ^ (r & 15u); }
+__device__ __forceinline__ uint32_t swz_tr(uint32_t r, uint32_t c) { return c ^ ((r & 3u) << 2); }
+
+// Copy a tile of `rows` x 256 B (row stride `stride` bytes in global memory) into LDS at `lds`
+// with the given swizzle, using nwaves waves. Rows past the resource range arrive as zeros.
+template <bool TR>
+__device__ __forceinline__ void tile_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t stride, char* lds,
+                                            int rows, int wave, int nwaves, int lane) {
+  // one wave instruction covers 4 rows (1 KB); lane -> row 4n + lane/16, stored chunk lane%16
+  for (int n = wave; n < rows / 4; n += nwaves) {
+    uint32_t row = 4 * n + (lane >> 4);
+    uint32_t pos = lane & 15;
+    uint32_t src_chunk = TR ? swz_tr(row, pos) : swz_row(row, pos);
+    buf_load_lds16(r, lds + 1024 * n, row * stride + src_chunk * 16);
+  }
+}
+
+// Address of a 16-byte row-read operand: row r, logical chunk c.
+__device__ __forceinline__ const char* row_addr(const char* tile, uint32_t r, uint32_t c) {
+  return tile + r * 256 + swz_row(r, c) * 16;
+}
+
+// Address for ds_read_b64_tr_b16 on a transpose-read tile: logical element (row r, column col),
+// col a multiple of 4.
+__device__ __forceinline__ const char* tr_addr(const char* tile, uint32_t r, uint32_t col) {
+  uint32_t byte = col * 2;
+  return tile + r * 256 + swz_tr(r, byte >> 4) * 16 + (byte & 15);
+}
+
+// 32x32x16 operand "transposed" from a row-major [key][col] transpose-read tile: the lane gets
+// X[key_lo + 0..3][col] in elements 0..3 and X[key_hi + 0..3][col] in elements 4..7, where
+// col = c0 + (lane % 16 within the 16-lane group) and the caller passes the per-half key bases.
+// Lane r of a 16-lane group addresses row key + r/4, columns c0 + 4*(r%4) .. +3.
+__device__ __forceinline__ bf16x8 tr_operand(const char* tile, uint32_t key_lo, uint32_t key_hi,
+                                             uint32_t c0, uint32_t lane16) {
+  uint32_t dr = lane16 >> 2, dc = 4 * (lane16 & 3);
+  i16x4 a = lds_tr16(tr_addr(tile, key_lo + dr, c0 + dc));
+  i16x4 b = lds_tr16(tr_addr(tile, key_hi + dr, c0 + dc));
+  return join_tr(a, b);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ uint32_t float_order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace pisa

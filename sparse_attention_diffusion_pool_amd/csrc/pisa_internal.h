@@ -1,0 +1,69 @@
+// Internal interface between the C-ABI host layer (pisa_host.cpp) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pisa {
+
+// Blocks whose K^T V products one statistics workgroup sums before writing a partial of H-bar.
+constexpr int kStatsChunk = 16;
+
+struct Dims {
+  int H;
+  int L;
+  int d;
+  int B;
+  int Nb;      // ceil(L / B)
+  int k;       // critical blocks per query block
+  int n_last;  // rows of the last block
+  int NC;      // ceil(Nb / kStatsChunk): partial H-bar sums per head
+  int Nbp;     // Nb rounded up to a multiple of B (pooled-token tiles)
+  float scale; // softmax scale applied to q
+  int routing; // 0 covariance-aware, 1 plain
+  int phases;  // bit mask: 1 exact, 2 zeroth order, 4 first order
+  int dtype;   // 0 bf16, 1 fp32
+};
+
+// Device pointers into the attached workspace.
+struct Work {
+  float* qbar;      // [H][Nb][d]   pooled scaled queries (mean of scale*q over the block)
+  float* kbar;      // [H][Nb][d]   key centroids
+  float* vsum;      // [H][Nb][d]   value sums
+  float* G;         // [H][NC][d][d] partial sums of K_j^T V_j
+  float* hbar;      // [H][d][d]    H-bar
+  float* M;         // [H][Nb]      ||H_j - H-bar||_F
+  void* kbar_lo;    // bf16 [H][Nbp][d] centroids, zero rows past Nb      (bf16 path only)
+  void* vbar_lo;    // bf16 [H][Nbp][d] value means, zero rows past Nb    (bf16 path only)
+  void* hbarT_lo;   // bf16 [H][d][d]   transpose of H-bar                (bf16 path only)
+  int32_t* idx;     // [H][Nb][k]   ascending critical block indices
+};
+
+struct Layout {
+  size_t qbar, kbar, vsum, G, hbar, M, kbar_lo, vbar_lo, hbarT_lo, idx, total;
+};
+
+Layout workspace_layout(const Dims& dm);
+Work workspace_pointers(const Dims& dm, void* base);
+
+// Statistics (precompute), routing and the fused attention kernel launchers. Each returns the
+// first HIP error of its launches.
+hipError_t launch_stats_pass(const Dims& dm, const Work& w, const void* Q, const void* K,
+                             const void* V, hipStream_t s);      // centroids, sums, K^T V partials
+hipError_t launch_stats_finalize(const Dims& dm, const Work& w, hipStream_t s);  // H-bar, lo copies
+hipError_t launch_stats_cov(const Dims& dm, const Work& w, const void* K, const void* V,
+                            hipStream_t s);                       // M_j
+hipError_t launch_route(const Dims& dm, const Work& w, hipStream_t s);
+hipError_t launch_attend(const Dims& dm, const Work& w, const void* Q, const void* K,
+                         const void* V, void* out, hipStream_t s);
+
+// Per-dtype implementations.
+hipError_t launch_stats_pass_bf16(const Dims&, const Work&, const void*, const void*, const void*, hipStream_t);
+hipError_t launch_stats_cov_bf16(const Dims&, const Work&, const void*, const void*, hipStream_t);
+hipError_t launch_stats_pass_f32(const Dims&, const Work&, const void*, const void*, const void*, hipStream_t);
+hipError_t launch_stats_cov_f32(const Dims&, const Work&, const void*, const void*, hipStream_t);
+hipError_t launch_attend_bf16(const Dims&, const Work&, const void*, const void*, const void*, void*, hipStream_t);
+hipError_t launch_attend_f32(const Dims&, const Work&, const void*, const void*, const void*, void*, hipStream_t);
+
+}  // namespace pisa

@@ -1,0 +1,351 @@
+// Block statistics for PISA (the precompute step of the fused kernel described on the
+// gist.science summary of the PISA paper, section 2 "Hardware implementation"; the statistics
+// themselves follow section 2 "Core algorithm" - centroid and value sum of every block - and
+// "Covariance-aware routing" - the block first-order matrices H_j, their mean H-bar and
+// M_j = ||H_j - H-bar||).
+//
+// Pass A (one workgroup per 16 consecutive blocks of a head): column sums of Q, K, V per block
+// (pooled scaled query, key centroid, value sum) and the partial sum of K_j^T V_j over its
+// blocks. Finalize (per head): H-bar = (sum_j K_j^T V_j - sum_j kbar_j (sum V_j)^T) / N_b, using
+// H_j = K_j^T V_j - n_j kbar_j vbar_j^T; bf16 copies of the pooled tokens and of H-bar^T for the
+// attention kernel. Covariance pass (one workgroup per block): H_j again, then
+// M_j = ||H_j - H-bar||_F.
+//
+// bf16 inputs: K_j^T V_j on v_mfma_f32_32x32x16_bf16 (products of bf16 values are exact in fp32,
+// accumulation fp32); both operands come from row-major LDS tiles through ds_read_b64_tr_b16.
+// fp32 inputs: plain fp32 FMA.
+#include "dev_common.h"
+#include "pisa_internal.h"
+
+namespace pisa {
+namespace {
+
+__device__ __forceinline__ void unpack_bf16x8(u32x4 x, float* f) {
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(x[i] << 16);
+    f[2 * i + 1] = __uint_as_float(x[i] & 0xffff0000u);
+  }
+}
+
+// K^T V of one B x 128 block held in two transpose-read LDS tiles; wave w owns rows 32w..32w+31
+// of the 128 x 128 product: acc[ct] covers columns 32ct..32ct+31.
+template <int BLK>
+__device__ __forceinline__ void ktv_mfma(const char* Ks, const char* Vs, f32x16 acc[4], int wave, int lane) {
+  const uint32_t hh = lane >> 5, g16 = (lane >> 4) & 1, l16 = lane & 15;
+#pragma unroll
+  for (int ks = 0; ks < BLK / 16; ++ks) {
+    const uint32_t klo = 16 * ks + 8 * hh;
+    bf16x8 a = tr_operand(Ks, klo, klo + 4, 32 * wave + 16 * g16, l16);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      bf16x8 b = tr_operand(Vs, klo, klo + 4, 32 * ct + 16 * g16, l16);
+      acc[ct] = mfma32(a, b, acc[ct]);
+    }
+  }
+}
+
+template <int BLK>
+__global__ __launch_bounds__(256) void stats_pass_bf16(Dims dm, Work w, const __bf16* __restrict__ Q,
+                                                       const __bf16* __restrict__ K,
+                                                       const __bf16* __restrict__ V) {
+  __shared__ __attribute__((aligned(1024))) char Ks[BLK * 256];
+  __shared__ __attribute__((aligned(1024))) char Vs[BLK * 256];
+  __shared__ float red[4][3][128];
+  const int h = blockIdx.y, c = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int j0 = c * kStatsChunk, j1 = min(dm.Nb, j0 + kStatsChunk);
+  const size_t head = (size_t)h * dm.L * 128;
+  f32x16 acc[4];
+  for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x16{};
+  const int p = tid & 15, rg = tid >> 4;  // column chunk (8 columns) and row group for the sums
+
+  for (int j = j0; j < j1; ++j) {
+    const int n = (j == dm.Nb - 1) ? dm.n_last : dm.B;
+    const size_t r0 = head + (size_t)j * dm.B * 128;
+    __amdgpu_buffer_rsrc_t rk = make_rsrc(K + r0, n * 256);
+    __amdgpu_buffer_rsrc_t rv = make_rsrc(V + r0, n * 256);
+    __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + r0, n * 256);
+    tile_to_lds<true>(rk, 256, Ks, BLK, wave, 4, lane);
+    tile_to_lds<true>(rv, 256, Vs, BLK, wave, 4, lane);
+    float qs[8] = {0, 0, 0, 0, 0, 0, 0, 0}, ks8[8] = {0, 0, 0, 0, 0, 0, 0, 0}, vs8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int r = rg; r < BLK; r += 16) {
+      float f[8];
+      unpack_bf16x8(buf_load16(rq, r * 256 + p * 16), f);
+      for (int e = 0; e < 8; ++e) qs[e] += f[e];
+    }
+    wait_vmem();
+    __syncthreads();
+    for (int r = rg; r < BLK; r += 16) {
+      float f[8];
+      unpack_bf16x8(*reinterpret_cast<const u32x4*>(Ks + r * 256 + swz_tr(r, p) * 16), f);
+      for (int e = 0; e < 8; ++e) ks8[e] += f[e];
+      unpack_bf16x8(*reinterpret_cast<const u32x4*>(Vs + r * 256 + swz_tr(r, p) * 16), f);
+      for (int e = 0; e < 8; ++e) vs8[e] += f[e];
+    }
+    for (int e = 0; e < 8; ++e) {
+      qs[e] += __shfl_xor(qs[e], 16);
+      qs[e] += __shfl_xor(qs[e], 32);
+      ks8[e] += __shfl_xor(ks8[e], 16);
+      ks8[e] += __shfl_xor(ks8[e], 32);
+      vs8[e] += __shfl_xor(vs8[e], 16);
+      vs8[e] += __shfl_xor(vs8[e], 32);
+    }
+    if (lane < 16) {
+      for (int e = 0; e < 8; ++e) {
+        red[wave][0][8 * p + e] = qs[e];
+        red[wave][1][8 * p + e] = ks8[e];
+        red[wave][2][8 * p + e] = vs8[e];
+      }
+    }
+    ktv_mfma<BLK>(Ks, Vs, acc, wave, lane);
+    __syncthreads();
+    if (tid < 128) {
+      const float inv = 1.0f / (float)n;
+      float sq = red[0][0][tid] + red[1][0][tid] + red[2][0][tid] + red[3][0][tid];
+      float sk = red[0][1][tid] + red[1][1][tid] + red[2][1][tid] + red[3][1][tid];
+      float sv = red[0][2][tid] + red[1][2][tid] + red[2][2][tid] + red[3][2][tid];
+      const size_t o = ((size_t)h * dm.Nb + j) * 128 + tid;
+      w.qbar[o] = sq * dm.scale * inv;
+      w.kbar[o] = sk * inv;
+      w.vsum[o] = sv;
+    }
+  }
+  // partial sum of K_j^T V_j over this chunk: G[h][c][a][b]
+  float* G = w.G + ((size_t)h * dm.NC + c) * 128 * 128;
+  const int hh = lane >> 5, l32 = lane & 31;
+  for (int ct = 0; ct < 4; ++ct)
+    for (int x = 0; x < 16; ++x) {
+      const int a = 32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3);
+      G[a * 128 + 32 * ct + l32] = acc[ct][x];
+    }
+}
+
+template <int BLK>
+__global__ __launch_bounds__(256) void stats_cov_bf16(Dims dm, Work w, const __bf16* __restrict__ K,
+                                                      const __bf16* __restrict__ V) {
+  __shared__ __attribute__((aligned(1024))) char Ks[BLK * 256];
+  __shared__ __attribute__((aligned(1024))) char Vs[BLK * 256];
+  __shared__ float red[4];
+  const int h = blockIdx.y, j = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = (j == dm.Nb - 1) ? dm.n_last : dm.B;
+  const size_t r0 = (size_t)h * dm.L * 128 + (size_t)j * dm.B * 128;
+  tile_to_lds<true>(make_rsrc(K + r0, n * 256), 256, Ks, BLK, wave, 4, lane);
+  tile_to_lds<true>(make_rsrc(V + r0, n * 256), 256, Vs, BLK, wave, 4, lane);
+  wait_vmem();
+  __syncthreads();
+  f32x16 acc[4];
+  for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x16{};
+  ktv_mfma<BLK>(Ks, Vs, acc, wave, lane);
+  const int hh = lane >> 5, l32 = lane & 31;
+  const float* kb = w.kbar + ((size_t)h * dm.Nb + j) * 128;
+  const float* vs = w.vsum + ((size_t)h * dm.Nb + j) * 128;
+  const float* hb = w.hbar + (size_t)h * 128 * 128;
+  float ss = 0.f;
+  for (int ct = 0; ct < 4; ++ct) {
+    const int b = 32 * ct + l32;
+    const float vb = vs[b];
+    for (int x = 0; x < 16; ++x) {
+      const int a = 32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3);
+      const float hv = acc[ct][x] - kb[a] * vb - hb[a * 128 + b];
+      ss += hv * hv;
+    }
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  if (tid == 0) w.M[(size_t)h * dm.Nb + j] = sqrtf(red[0] + red[1] + red[2] + red[3]);
+}
+
+// ---------------------------------------------------------------------------------------------
+// fp32 inputs: plain FMA. Each thread owns a P x P patch of the D x D product (P = D / 16).
+// ---------------------------------------------------------------------------------------------
+
+template <int D, bool COV>
+__global__ __launch_bounds__(256) void stats_f32(Dims dm, Work w, const float* __restrict__ Q,
+                                                 const float* __restrict__ K, const float* __restrict__ V) {
+  constexpr int P = D / 16;
+  constexpr int SUB = 32;  // rows per LDS sub-tile
+  __shared__ float Ks[SUB][D + 4];
+  __shared__ float Vs[SUB][D + 4];
+  __shared__ float red[256 / 64];
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int a0 = P * (tid / 16), b0 = P * (tid % 16);
+  int j0, j1;
+  if (COV) {
+    j0 = blockIdx.x;
+    j1 = j0 + 1;
+  } else {
+    j0 = blockIdx.x * kStatsChunk;
+    j1 = min(dm.Nb, j0 + kStatsChunk);
+  }
+  float acc[P][P];
+  for (int x = 0; x < P; ++x)
+    for (int y = 0; y < P; ++y) acc[x][y] = 0.f;
+  for (int j = j0; j < j1; ++j) {
+    const int n = (j == dm.Nb - 1) ? dm.n_last : dm.B;
+    const size_t r0 = (size_t)h * dm.L * D + (size_t)j * dm.B * D;
+    if (COV)
+      for (int x = 0; x < P; ++x)
+        for (int y = 0; y < P; ++y) acc[x][y] = 0.f;
+    if (!COV && tid < D) {
+      float sq = 0.f, sk = 0.f, sv = 0.f;
+      for (int r = 0; r < n; ++r) {
+        sq += Q[r0 + (size_t)r * D + tid];
+        sk += K[r0 + (size_t)r * D + tid];
+        sv += V[r0 + (size_t)r * D + tid];
+      }
+      const size_t o = ((size_t)h * dm.Nb + j) * D + tid;
+      w.qbar[o] = sq * dm.scale / (float)n;
+      w.kbar[o] = sk / (float)n;
+      w.vsum[o] = sv;
+    }
+    for (int s0 = 0; s0 < n; s0 += SUB) {
+      __syncthreads();
+      for (int e = tid; e < SUB * D; e += 256) {
+        const int r = e / D, cc = e % D;
+        const bool ok = s0 + r < n;
+        Ks[r][cc] = ok ? K[r0 + (size_t)(s0 + r) * D + cc] : 0.f;
+        Vs[r][cc] = ok ? V[r0 + (size_t)(s0 + r) * D + cc] : 0.f;
+      }
+      __syncthreads();
+      for (int r = 0; r < SUB; ++r)
+        for (int x = 0; x < P; ++x) {
+          const float kv = Ks[r][a0 + x];
+          for (int y = 0; y < P; ++y) acc[x][y] += kv * Vs[r][b0 + y];
+        }
+    }
+    if (COV) {
+      const float* kb = w.kbar + ((size_t)h * dm.Nb + j) * D;
+      const float* vs = w.vsum + ((size_t)h * dm.Nb + j) * D;
+      const float* hb = w.hbar + (size_t)h * D * D;
+      float ss = 0.f;
+      for (int x = 0; x < P; ++x)
+        for (int y = 0; y < P; ++y) {
+          const float hv = acc[x][y] - kb[a0 + x] * vs[b0 + y] - hb[(a0 + x) * D + b0 + y];
+          ss += hv * hv;
+        }
+      ss = wave_sum(ss);
+      if ((tid & 63) == 0) red[tid >> 6] = ss;
+      __syncthreads();
+      if (tid == 0) w.M[(size_t)h * dm.Nb + j] = sqrtf(red[0] + red[1] + red[2] + red[3]);
+    }
+  }
+  if (!COV) {
+    float* G = w.G + ((size_t)h * dm.NC + blockIdx.x) * D * D;
+    for (int x = 0; x < P; ++x)
+      for (int y = 0; y < P; ++y) G[(a0 + x) * D + b0 + y] = acc[x][y];
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Finalize: H-bar, and (bf16 path) bf16 pooled tokens and H-bar^T.
+// Grid (16, H): workgroup x owns rows 8x..8x+7 of H-bar for d = 128 (4x..4x+3 for d = 64) and
+// converts the pooled rows j = x, x + 16, ...
+// ---------------------------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(256) void stats_finalize(Dims dm, Work w) {
+  constexpr int E = D * D / 16 / 256;  // entries per thread
+  const int h = blockIdx.y, x = blockIdx.x, tid = threadIdx.x;
+  const float* kb = w.kbar + (size_t)h * dm.Nb * D;
+  const float* vs = w.vsum + (size_t)h * dm.Nb * D;
+  const float* G = w.G + (size_t)h * dm.NC * D * D;
+  const int a_base = x * (D / 16);
+  int a[E], b[E];
+  float g[E], corr[E];
+  for (int e = 0; e < E; ++e) {
+    const int lin = tid + 256 * e;
+    a[e] = a_base + lin / D;
+    b[e] = lin % D;
+    g[e] = 0.f;
+    corr[e] = 0.f;
+  }
+  for (int c = 0; c < dm.NC; ++c)
+    for (int e = 0; e < E; ++e) g[e] += G[(size_t)c * D * D + a[e] * D + b[e]];
+  for (int j = 0; j < dm.Nb; ++j)
+    for (int e = 0; e < E; ++e) corr[e] += kb[(size_t)j * D + a[e]] * vs[(size_t)j * D + b[e]];
+  const float inv_nb = 1.0f / (float)dm.Nb;
+  for (int e = 0; e < E; ++e) {
+    const float v = (g[e] - corr[e]) * inv_nb;
+    w.hbar[(size_t)h * D * D + a[e] * D + b[e]] = v;
+    if (dm.dtype == 0) reinterpret_cast<__bf16*>(w.hbarT_lo)[(size_t)h * D * D + b[e] * D + a[e]] = (__bf16)v;
+  }
+  if (dm.dtype == 0) {
+    __bf16* kl = reinterpret_cast<__bf16*>(w.kbar_lo) + (size_t)h * dm.Nbp * D;
+    __bf16* vl = reinterpret_cast<__bf16*>(w.vbar_lo) + (size_t)h * dm.Nbp * D;
+    for (int j = x + 16 * (tid / D); j < dm.Nbp; j += 16 * (256 / D)) {
+      const int cc = tid % D;
+      float kv = 0.f, vv = 0.f;
+      if (j < dm.Nb) {
+        const float n = (j == dm.Nb - 1) ? (float)dm.n_last : (float)dm.B;
+        kv = kb[(size_t)j * D + cc];
+        vv = vs[(size_t)j * D + cc] / n;
+      }
+      kl[(size_t)j * D + cc] = (__bf16)kv;
+      vl[(size_t)j * D + cc] = (__bf16)vv;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_stats_pass_bf16(const Dims& dm, const Work& w, const void* Q, const void* K, const void* V,
+                                  hipStream_t s) {
+  dim3 grid(dm.NC, dm.H);
+  auto q = static_cast<const __bf16*>(Q);
+  auto k = static_cast<const __bf16*>(K);
+  auto v = static_cast<const __bf16*>(V);
+  if (dm.B == 128)
+    hipLaunchKernelGGL(stats_pass_bf16<128>, grid, dim3(256), 0, s, dm, w, q, k, v);
+  else
+    hipLaunchKernelGGL(stats_pass_bf16<64>, grid, dim3(256), 0, s, dm, w, q, k, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_stats_cov_bf16(const Dims& dm, const Work& w, const void* K, const void* V, hipStream_t s) {
+  dim3 grid(dm.Nb, dm.H);
+  auto k = static_cast<const __bf16*>(K);
+  auto v = static_cast<const __bf16*>(V);
+  if (dm.B == 128)
+    hipLaunchKernelGGL(stats_cov_bf16<128>, grid, dim3(256), 0, s, dm, w, k, v);
+  else
+    hipLaunchKernelGGL(stats_cov_bf16<64>, grid, dim3(256), 0, s, dm, w, k, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_stats_pass_f32(const Dims& dm, const Work& w, const void* Q, const void* K, const void* V,
+                                 hipStream_t s) {
+  dim3 grid(dm.NC, dm.H);
+  auto q = static_cast<const float*>(Q);
+  auto k = static_cast<const float*>(K);
+  auto v = static_cast<const float*>(V);
+  if (dm.d == 128)
+    hipLaunchKernelGGL((stats_f32<128, false>), grid, dim3(256), 0, s, dm, w, q, k, v);
+  else
+    hipLaunchKernelGGL((stats_f32<64, false>), grid, dim3(256), 0, s, dm, w, q, k, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_stats_cov_f32(const Dims& dm, const Work& w, const void* K, const void* V, hipStream_t s) {
+  dim3 grid(dm.Nb, dm.H);
+  auto k = static_cast<const float*>(K);
+  auto v = static_cast<const float*>(V);
+  if (dm.d == 128)
+    hipLaunchKernelGGL((stats_f32<128, true>), grid, dim3(256), 0, s, dm, w, nullptr, k, v);
+  else
+    hipLaunchKernelGGL((stats_f32<64, true>), grid, dim3(256), 0, s, dm, w, nullptr, k, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_stats_finalize(const Dims& dm, const Work& w, hipStream_t s) {
+  dim3 grid(16, dm.H);
+  if (dm.d == 128)
+    hipLaunchKernelGGL(stats_finalize<128>, grid, dim3(256), 0, s, dm, w);
+  else
+    hipLaunchKernelGGL(stats_finalize<64>, grid, dim3(256), 0, s, dm, w);
+  return hipGetLastError();
+}
+
+}  // namespace pisa

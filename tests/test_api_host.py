@@ -1,0 +1,133 @@
+"""C-ABI host paths (no GPU needed): the library loads, exports every symbol include/pisa.h declares,
+validates arguments before any launch, reports the plan's derived sizes, and never aborts."""
+
+import ctypes
+import math
+import subprocess
+
+import pytest
+
+from oracle import pisa_oracle as po
+from sparse_attention_diffusion_pool_amd import _lib as L
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = L.header_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert set(names) <= exported
+
+
+def _plan(lib, L_, H, d, B, keep):
+    h = ctypes.c_void_p()
+    st = lib.pisa_plan(L_, H, d, B, keep, ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 1, 128, 128, 0.5), 1), ((10, 0, 128, 128, 0.5), 1), ((10, 1, 128, 128, 0.0), 1),
+    ((10, 1, 128, 128, 1.5), 1), ((10, 1, 128, 128, float("nan")), 1), ((10, 1, 96, 128, 0.5), 2),
+    ((10, 1, 128, 32, 0.5), 2), ((1 << 30, 4, 128, 128, 0.5), 2), ((128 * 8193, 1, 128, 128, 0.5), 2),
+])
+def test_invalid_plans(lib, args, status):
+    st, h = _plan(lib, *args)
+    assert st == status, L.last_error()
+    assert h.value is None
+    assert L.last_error()
+
+
+def test_null_plan_pointer(lib):
+    assert lib.pisa_plan(10, 1, 128, 128, 0.5, None) == 1
+
+
+@pytest.mark.parametrize("Lq,H,d,B,keep", [(75600, 40, 128, 128, 0.10), (119056, 24, 128, 128, 0.08),
+                                           (1024, 2, 64, 64, 0.25), (4608, 24, 128, 64, 0.25),
+                                           (32760, 40, 128, 128, 0.125), (100, 3, 128, 128, 0.3),
+                                           (129, 1, 64, 128, 1.0)])
+def test_plan_info_matches_formulas(Lq, H, d, B, keep):
+    p = L.Plan(Lq, H, d, B, keep)
+    inf = p.info()
+    nb = po.n_blocks(Lq, B)
+    assert inf["n_blocks"] == nb
+    assert inf["k"] == po.top_k_count(keep, nb)
+    assert inf["n_last"] == Lq - (nb - 1) * B
+    assert inf["dtype"] == (0 if d == 128 else 1)
+    assert math.isclose(inf["scale"], 1 / math.sqrt(d), rel_tol=1e-7)
+    assert inf["workspace_bytes"] % 256 == 0 and inf["workspace_bytes"] > 0
+    assert inf["flops_first"] == H * 2 * Lq * d * d
+    assert inf["flops_route"] == H * 2 * nb * nb * d
+    p.destroy()
+
+
+def test_options(lib):
+    p = L.Plan(1000, 2, 128, 128, 0.25)
+    w0 = p.info()["workspace_bytes"]
+    lib_ = L.load()
+    assert lib_.pisa_plan_set(p.handle, L.OPT_DTYPE, 1.0) == 0
+    assert p.info()["dtype"] == 1 and p.info()["workspace_bytes"] != w0
+    assert lib_.pisa_plan_set(p.handle, L.OPT_DTYPE, 2.0) == 1
+    assert lib_.pisa_plan_set(p.handle, L.OPT_SCALE, -1.0) == 1
+    assert lib_.pisa_plan_set(p.handle, L.OPT_SCALE, 0.5) == 0 and p.info()["scale"] == 0.5
+    assert lib_.pisa_plan_set(p.handle, L.OPT_ROUTING, 1.0) == 0 and p.info()["routing"] == 1
+    assert lib_.pisa_plan_set(p.handle, L.OPT_PHASES, 2.0) == 1  # exact phase is mandatory
+    assert lib_.pisa_plan_set(p.handle, L.OPT_PHASES, 1.5) == 1
+    assert lib_.pisa_plan_set(p.handle, L.OPT_PHASES, 1.0) == 0 and p.info()["phases"] == 1
+    assert lib_.pisa_plan_set(p.handle, 99, 1.0) == 1
+    q = L.Plan(1000, 2, 64, 64, 0.25)
+    assert lib_.pisa_plan_set(q.handle, L.OPT_DTYPE, 0.0) == 2  # bf16 needs d = 128
+
+
+def test_workspace_and_pointer_checks(lib):
+    p = L.Plan(1000, 2, 128, 128, 0.25)
+    need = p.info()["workspace_bytes"]
+    h = p.handle
+    st = lib.pisa_forward(h, 16, 32, 48, 64, None)
+    assert st == 4  # no workspace
+    assert lib.pisa_plan_attach_workspace(h, None, need) == 4
+    assert lib.pisa_plan_attach_workspace(h, 256 * 3 + 16, need) == 4  # misaligned
+    assert lib.pisa_plan_attach_workspace(h, 256 * 1000, need - 1) == 4  # too small
+    assert lib.pisa_plan_attach_workspace(h, 256 * 1000, need) == 0
+    # argument checks happen before the device check
+    assert lib.pisa_forward(h, None, 32, 48, 64, None) == 1
+    assert lib.pisa_forward(h, 16, 32, 48, None, None) == 1
+    assert lib.pisa_forward(h, 17, 32, 48, 1 << 40, None) == 1  # misaligned Q
+    nbytes = 2 * 1000 * 128 * 2
+    assert lib.pisa_forward(h, 1 << 20, 1 << 30, 1 << 31, (1 << 20) + nbytes - 16, None) == 1  # overlaps Q
+
+
+def test_forward_without_device_reports_device_error(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    p = L.Plan(1000, 2, 128, 128, 0.25)
+    assert lib.pisa_plan_attach_workspace(p.handle, 256 * 1000, p.info()["workspace_bytes"]) == 0
+    for call in (lambda: lib.pisa_forward(p.handle, 1 << 20, 1 << 30, 1 << 31, 1 << 32, None),
+                 lambda: lib.pisa_forward_route(p.handle, None),
+                 lambda: lib.pisa_debug_copy_selection(p.handle, 1 << 20, None)):
+        assert call() == 5
+        assert "device" in L.last_error()
+
+
+def test_destroy_twice_and_foreign_handles(lib):
+    st, h = _plan(lib, 1000, 2, 128, 128, 0.25)
+    assert st == 0
+    assert lib.pisa_plan_destroy(h) == 0
+    assert lib.pisa_plan_destroy(h) == 3
+    assert lib.pisa_plan_destroy(None) == 3
+    info = L.PlanInfo()
+    assert lib.pisa_plan_info(h, ctypes.byref(info)) == 3
+    assert lib.pisa_forward(h, 16, 32, 48, 64, None) == 3
+
+
+def test_status_strings(lib):
+    for s, name in L.STATUS.items():
+        assert lib.pisa_status_string(s).decode() == name
+    assert lib.pisa_status_string(42).decode() == "PISA_ERR_UNKNOWN"
