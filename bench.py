@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of the PISA forward pass (libpisa) on one MI355X.
+
+A step is one whole pass of the hot path over the workload: block statistics, routing and the
+fused piecewise attention (pisa_forward_stats + pisa_forward_route + pisa_forward_attend, which
+together are pisa_forward). Inputs are generated once (seeded, synthetic) and resident in HBM
+before the timed region. HIP events recorded on the library's stream between the stages give the
+per-stage time of every step; the attention kernel's average duration feeds the roofline.
+
+Prints one JSON line. Default workload: the Wan2.1-14B-like 720p layer (40 heads, L = 75600,
+d = 128, B = 128, keep 10%, bf16).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "PISA attn fwd ms/call + achieved TFLOP/s vs bf16 MFMA peak, Wan-720p shape"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_F32_VALU_TFLOPS = 157.3
+PEAK_HBM_GBPS = 8000.0
+ATTEND_SRC = os.path.join(ROOT, "sparse_attention_diffusion_pool_amd", "csrc", "attend_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_bf16_wan720p_traffic.json")
+
+
+def source_sha(path: str) -> str:
+    files = [path, os.path.join(os.path.dirname(path), "dev_common.h")]
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_flops(idx: np.ndarray, L: int, d: int, B: int, phases: int) -> dict:
+    """Executed FLOPs of one call from the actual selection idx [H, N_b, k]: exact part
+    4 n_i n_j d per selected pair, zeroth-order part 4 n_i |U_i| d, first-order 2 L d^2 per head,
+    statistics 2 x 2 L d^2 per head (K^T V for H-bar and again for M_j), scores 2 N_b^2 d."""
+    H, nb, kk = idx.shape
+    n = np.full(nb, B, dtype=np.float64)
+    n[-1] = L - (nb - 1) * B
+    n_sel = n[idx].sum(axis=2)               # [H, N_b]: sum of n_j over S_i
+    exact = float((4.0 * d * n[None, :] * n_sel).sum())
+    tail = kk < nb and (phases & 2)
+    zeroth = float(4.0 * d * (n.sum() * (nb - kk)) * H) if tail else 0.0
+    first = float(2.0 * L * d * d * H) if tail and (phases & 4) else 0.0
+    stats = float(4.0 * L * d * d * H)
+    route = float(2.0 * nb * nb * d * H)
+    return {"exact": exact, "zeroth": zeroth, "first": first, "attend": exact + zeroth + first,
+            "stats": stats, "route": route, "total": exact + zeroth + first + stats + route}
+
+
+def dense_rows(q, k, v, rows, scale):
+    """softmax(scale q K^T) V for the given rows of one head, float64 on the host (quality check)."""
+    import torch
+    qq = q[rows].to(torch.float64) * scale
+    s = qq @ k.to(torch.float64).T
+    p = torch.softmax(s, dim=1)
+    return p @ v.to(torch.float64)
+
+
+def cpu_baseline(w, heads, sample_note):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload (whole heads)."""
+    from oracle import pisa_oracle as po
+    from workloads import head_inputs, to_float64
+    cores = len(os.sched_getaffinity(0))
+    flops = 0.0
+    secs = 0.0
+    for h in heads:
+        q, k, v = (to_float64(t) for t in head_inputs(w, h))
+        t0 = time.perf_counter()
+        r = po.pisa_head(q, k, v, w.B, w.keep)
+        secs += time.perf_counter() - t0
+        f = po.executed_flops(w.L, w.d, w.B, r["S"])
+        flops += f["total"]
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": sample_note, "seconds": secs, "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3, help="index into workloads.CONFIGS")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-quality", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=2)
+    ap.add_argument("--phases", type=int, default=7)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU "
+              "path (heads would shard across GPUs with no exchange); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_attention_diffusion_pool_amd import _lib as L
+    from workloads import CONFIGS, layer_inputs
+
+    w = CONFIGS[args.workload]
+    t_gen = time.perf_counter()
+    q, k, v = layer_inputs(w)
+    t_gen = time.perf_counter() - t_gen
+    dev = torch.device("cuda", 0)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    dtype = L.DTYPE_BF16 if w.dtype == "bf16" else L.DTYPE_F32
+    plan = L.Plan(w.L, w.H, w.d, w.B, w.keep, dtype=dtype, phases=args.phases)
+    plan.attach_workspace(device=dev)
+    info = plan.info()
+    out = torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+    print(f"[bench] {w.name}: generated in {t_gen:.1f}s; N_b={info['n_blocks']} k={info['k']}", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        plan.forward(qd, kd, vd, out, stream)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for s in range(K):
+        ev[s][0].record(stream)
+        plan.forward_stats(qd, kd, vd, stream)
+        ev[s][1].record(stream)
+        plan.forward_route(stream)
+        ev[s][2].record(stream)
+        plan.forward_attend(qd, kd, vd, out, stream)
+        ev[s][3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    step_ms = np.array([ev[s][0].elapsed_time(ev[s][3]) for s in range(K)])
+    stats_ms = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in range(K)])
+    route_ms = np.array([ev[s][1].elapsed_time(ev[s][2]) for s in range(K)])
+    attend_ms = np.array([ev[s][2].elapsed_time(ev[s][3]) for s in range(K)])
+    span_ms = ev[0][0].elapsed_time(ev[K - 1][3])
+    ms_per_step = span_ms / K
+
+    idx = torch.empty((w.H, info["n_blocks"], info["k"]), dtype=torch.int32, device=dev)
+    plan.debug_copy_selection(idx, stream)
+    torch.cuda.synchronize()
+    fl = algorithmic_flops(idx.cpu().numpy(), w.L, w.d, w.B, args.phases)
+    tflops = fl["total"] / (ms_per_step * 1e-3) / 1e12
+    attend_tflops = fl["attend"] / (attend_ms.mean() * 1e-3) / 1e12
+    stats_gbps = info["bytes_stats"] / (stats_ms.mean() * 1e-3) / 1e9
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_VALU_TFLOPS
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE) and w.cfg_id == 3:
+        tr = json.load(open(TRAFFIC_FILE))
+        if tr.get("source_sha") == source_sha(ATTEND_SRC):
+            traffic = tr.get("hbm_bytes_per_launch")
+
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded random-Fourier-feature Q/K of the layer's token grid, V ~ N(0,1))",
+        "config": {"workload": w.name, "H": w.H, "L": w.L, "d": w.d, "B": w.B, "keep": w.keep,
+                   "n_blocks": info["n_blocks"], "k": info["k"], "phases": args.phases},
+        "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "ms": {"step_median": round(float(np.median(step_ms)), 4), "step_min": round(float(step_ms.min()), 4),
+               "stats": round(float(stats_ms.mean()), 4), "route": round(float(route_ms.mean()), 4),
+               "attend": round(float(attend_ms.mean()), 4), "wall_per_step": round(wall / K * 1e3, 4)},
+        "executed_flops": fl,
+        "stats_hbm": {"bytes": info["bytes_stats"], "GBps": round(stats_gbps, 1),
+                      "frac": round(stats_gbps / PEAK_HBM_GBPS, 4)},
+        "roofline": {"kernel": "attend_bf16" if w.dtype == "bf16" else "attend_f32",
+                     "bound": "mfma" if w.dtype == "bf16" else "alu",
+                     "achieved": round(attend_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(attend_tflops / peak, 4), "traffic": traffic},
+    }
+
+    if not args.no_quality:
+        # quality check on sampled query blocks of 2 heads: relative L2 of PISA (this run's output)
+        # and of keep-or-drop (same kernel, exact phase only) against dense softmax attention
+        plan_drop = L.Plan(w.L, w.H, w.d, w.B, w.keep, dtype=dtype, phases=1)
+        plan_drop.attach_workspace(device=dev)
+        out_drop = torch.empty_like(qd)
+        plan_drop.forward(qd, kd, vd, out_drop, stream)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(0)
+        nb = info["n_blocks"]
+        num = {"pisa": 0.0, "drop": 0.0}
+        den = 0.0
+        for h in (0, w.H - 1):
+            for i in sorted(rng.choice(nb, size=min(8, nb), replace=False)):
+                rows = np.arange(i * w.B, min(w.L, (i + 1) * w.B))
+                ref = dense_rows(q[h], k[h], v[h], rows, info["scale"])
+                den += float((ref ** 2).sum())
+                for name, o in (("pisa", out), ("drop", out_drop)):
+                    got = o[h, rows[0]:rows[-1] + 1].to(torch.float64).cpu()
+                    num[name] += float(((got - ref) ** 2).sum())
+        res["quality"] = {"rel_l2_vs_dense": {"pisa": math.sqrt(num["pisa"] / den),
+                                              "keep_or_drop": math.sqrt(num["drop"] / den)},
+                          "sample": "16 query blocks (8 random in the first and last head), dense fp64"}
+        plan_drop.destroy()
+
+    if not args.no_cpu_baseline:
+        heads = list(range(min(args.cpu_heads, w.H)))
+        note = (f"{len(heads)} of {w.H} heads of {w.name}, every query block: statistics, routing, "
+                f"piecewise rows (NumPy fp64); TFLOP/s of the same executed-FLOP count")
+        res["cpu_baseline"] = cpu_baseline(w, heads, note)
+
+    plan.destroy()
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

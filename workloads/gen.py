@@ -157,27 +157,33 @@ def _head_fp64(w: Workload, h: int, phi: np.ndarray, child) -> Tuple[np.ndarray,
     return q, k, v
 
 
-def head_inputs(w: Workload, h: int, _cache={}) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+def head_inputs(w: Workload, h: int, phi: Optional[np.ndarray] = None
+                ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Q, K, V of head ``h`` as CPU tensors ``[L, d]`` in the workload dtype."""
     kids = _children(w)
-    key = (w, "phi")
-    phi = _cache.get(key)
     if phi is None:
-        _cache.clear()
         phi = _features(w, kids[0])
-        _cache[key] = phi
     q, k, v = _head_fp64(w, h, phi, kids[2 + h])
     return _round(q, w.dtype), _round(k, w.dtype), _round(v, w.dtype)
 
 
-def layer_inputs(w: Workload, heads: Optional[Iterable[int]] = None):
-    """Q, K, V as CPU tensors ``[H', L, d]`` (``H'`` = number of requested heads, default all)."""
+def layer_inputs(w: Workload, heads: Optional[Iterable[int]] = None, workers: int = 8):
+    """Q, K, V as CPU tensors ``[H', L, d]`` (``H'`` = number of requested heads, default all).
+    Heads are generated in a thread pool; each head's values depend only on its own stream."""
+    import concurrent.futures as cf
+
     heads = list(range(w.H)) if heads is None else list(heads)
     L, d = w.L, w.d
     out = [torch.empty((len(heads), L, d), dtype=w.torch_dtype) for _ in range(3)]
-    for n, h in enumerate(heads):
-        for dst, src in zip(out, head_inputs(w, h)):
+    phi = _features(w, _children(w)[0])
+
+    def fill(n_h):
+        n, h = n_h
+        for dst, src in zip(out, head_inputs(w, h, phi)):
             dst[n].copy_(src)
+
+    with cf.ThreadPoolExecutor(max_workers=max(1, workers)) as ex:
+        list(ex.map(fill, enumerate(heads)))
     return tuple(out)
 
 
