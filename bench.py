@@ -98,7 +98,20 @@ def main():
     ap.add_argument("--no-quality", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=2)
     ap.add_argument("--phases", type=int, default=7)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (scales the HBM byte counters)")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        n = 1 << 28
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read": 4 * n, "bytes_written": 4 * n}}))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU "

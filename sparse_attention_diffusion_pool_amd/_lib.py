@@ -72,6 +72,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    # torch-ROCm ships its own HIP runtime under the same soname: load torch first so that libpisa
+    # binds to the runtime that owns torch's device memory and streams (one runtime per process)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(path):
         raise RuntimeError(f"libpisa is not built ({path} missing): run "
                            "`python -m sparse_attention_diffusion_pool_amd.build`")

@@ -3,23 +3,26 @@
 // structure: exact blocks, then aggregated block vectors at zeroth order, then the global
 // first-order correction, all inside one online softmax).
 //
-// One workgroup per (head, query block), BLK/32 waves, wave w owning query rows 32w..32w+31.
-// Everything is computed transposed so that every per-query quantity lives in the lane that owns
-// the query (lane % 32):
-//   S^T = K_tile Q^T      A = K rows from LDS (16 B reads), B = Q^T held in registers
-//   O^T += V^T P^T        A = V^T via ds_read_b64_tr_b16 from the row-major V tile,
-//                         B = P^T straight from the S^T accumulators (converted to bf16)
-//   T^T = H-bar^T Q^T     phase 3, same routine as S^T with H-bar^T as the tile
-// Lanes l and l^32 hold the two halves of each query's keys (and of its output columns); the row
-// max is exchanged between them once per tile, the row sums at the end.
+// Work decomposition: one workgroup per (head, query block of BLK rows), BLK/32 waves; wave w owns
+// query rows 32 w .. 32 w + 31 and all keys. Two workgroups share a CU (64 KB of LDS each), so the
+// two waves on each SIMD belong to different workgroups: one's softmax overlaps the other's MFMAs.
 //
-// Phase 1: for j in S_i (ascending), K_j and V_j tiles are copied global -> LDS directly
-// (buffer loads with the range cut at the block's n_j rows, so ragged rows read as zero) and
-// processed flash-style with scores in the log2 domain (scale * log2 e folded into one FMA).
-// Phase 2: pooled tokens (kbar_j, vbar_j) in tiles of BLK, with additive bias log2 n_j, masked to
-// j in U_i (selection bit mask in LDS) and j < N_b; beta += p / n_j.
-// Phase 3: O += (beta * scale) (q H-bar).
-// Epilogue: out = O / l, rounded to bf16, transposed through LDS for 16-byte row stores.
+// Everything is computed transposed so that per-query state lives in the lane owning the query
+// (lane % 32; lanes l and l ^ 32 hold the two halves of the query's keys / output columns):
+//   S^T = K Q^T      A = K rows from LDS (16 B reads), B = Q^T held in registers
+//   O^T += V^T P^T   A = V^T via ds_read_b64_tr_b16 from the row-major V tile,
+//                    B = P^T straight from the S^T accumulators (converted to bf16)
+//   T^T = Hbar^T Q^T phase 3, same routine as S^T with H-bar^T as the tile
+//
+// Keys stream in steps of 64 through two LDS stages (K and V halves, 16 KB each): step s + 1 is
+// copied global -> LDS (buffer loads, rows past the block end read as zero) while step s is
+// computed. A key block of 128 rows takes two steps; the selected block list is staged in LDS.
+// Softmax runs in the log2 domain (scale * log2 e folded into one FMA); the accumulators are
+// rescaled only when a row's max grows by more than 2^8 (exact: numerator and denominator share
+// the stale reference, and p <= 256 stays far inside fp32/bf16 range).
+// Phase 2: pooled tokens (kbar_j, vbar_j), bias log2 n_j, masked to j in U_i (bit mask in LDS) and
+// j < N_b; beta += p / n_j. Phase 3: O += (beta * scale) (q H-bar).
+// Epilogue: out = O / l, rounded to bf16, staged through LDS for 16-byte row stores.
 #include "dev_common.h"
 #include "pisa_internal.h"
 
@@ -27,211 +30,310 @@ namespace pisa {
 namespace {
 
 constexpr int kMaskWords = (8192 + 128) / 32;  // N_b <= 8192, rounded up to a tile
+constexpr float kLazy = 8.0f;                   // rescale threshold (log2 units)
 
-// S^T for NT key subtiles of 32 rows: S[t] += Tile[32t + l32][:] . Q^T[:][query]
+// Per-lane LDS read offsets, computed once (relative to a tile's first row r0, r0 % 16 == 0):
+//   krd[s]: 16-byte row read of row r0 + l32, d-chunk 2 s + hh (row-read swizzle)
+//   vrd[dt]: transpose read of rows r0 + 4 hh + l16/4, columns 32 dt + 16 g16 + 4 (l16 % 4)
+//            (transpose-read swizzle); other key rows of the same lane differ by multiples of 4
+struct LaneOffsets {
+  uint32_t krd[8];
+  uint32_t vrd[4];
+};
+
+__device__ __forceinline__ LaneOffsets lane_offsets(uint32_t lane) {
+  const uint32_t hh = lane >> 5, l32 = lane & 31, g16 = (lane >> 4) & 1, l16 = lane & 15;
+  LaneOffsets o;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) o.krd[s] = l32 * 256 + swz_row(l32, 2 * s + hh) * 16;
+  const uint32_t dr = l16 >> 2;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const uint32_t byte = (32 * dt + 16 * g16 + 4 * (l16 & 3)) * 2;
+    o.vrd[dt] = (4 * hh + dr) * 256 + swz_tr(dr, byte >> 4) * 16 + (byte & 15);
+  }
+  return o;
+}
+
+// S^T for NT key subtiles of 32 rows starting at row r0 (r0 % 16 == 0):
+// S[t] = Tile[r0 + 32 t + l32][:] . Q^T
 template <int NT>
-__device__ __forceinline__ void qk_tile(const char* tile, const bf16x8 qreg[8], f32x16 S[NT], uint32_t l32,
-                                        uint32_t hh) {
+__device__ __forceinline__ void qk_tile(const char* tile, uint32_t r0, const bf16x8 qreg[8], f32x16 S[NT],
+                                        const LaneOffsets& lo) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) S[t] = f32x16{};
 #pragma unroll
   for (int s = 0; s < 8; ++s)
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(row_addr(tile, 32 * t + l32, 2 * s + hh));
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(tile + (r0 + 32 * t) * 256 + lo.krd[s]);
       S[t] = mfma32(a, qreg[s], S[t]);
     }
 }
 
-// O^T[dt] += V^T P^T over NT key subtiles.
+// O^T[dt] += V^T P^T over NT key subtiles starting at key r0 (r0 % 4 == 0).
 template <int NT>
-__device__ __forceinline__ void pv_tile(const char* Vs, const bf16x8 P[NT][2], f32x16 O[4], uint32_t hh,
-                                        uint32_t g16, uint32_t l16) {
+__device__ __forceinline__ void pv_tile(const char* Vs, uint32_t r0, const bf16x8 P[NT][2], f32x16 O[4],
+                                        const LaneOffsets& lo) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const uint32_t klo = 32 * t + 16 * u + 4 * hh;
-        const bf16x8 a = tr_operand(Vs, klo, klo + 8, 32 * dt + 16 * g16, l16);
-        O[dt] = mfma32(a, P[t][u], O[dt]);
+        const char* base = Vs + (r0 + 32 * t + 16 * u) * 256 + lo.vrd[dt];
+        const i16x4 x = lds_tr16(base);
+        const i16x4 y = lds_tr16(base + 8 * 256);
+        O[dt] = mfma32(join_tr(x, y), P[t][u], O[dt]);
       }
 }
 
-// Workgroup id -> logical work item, so that each of the 8 XCDs (which receive workgroup ids
-// round-robin) walks a contiguous range of (head, query block) items.
-__device__ __forceinline__ int xcd_remap(int bid, int n) {
-  const int per = n / 8, rem = n % 8;
-  const int x = bid % 8, q = bid / 8;
-  return x * per + min(x, rem) + q;
+// Workgroup id -> work item. Workgroup ids go to the 8 XCDs round-robin and start roughly in id
+// order; in each super-chunk of 8 * kRun consecutive ids, XCD x gets kRun consecutive items
+// (neighbouring query blocks of one head: their selected key blocks overlap, so they share the
+// XCD's L2), and all XCDs work on the same head at a time (its K and V stay in the last-level
+// cache).
+constexpr int kRun = 64;
+__device__ __forceinline__ int item_of(int bid, int n) {
+  constexpr int chunk = 8 * kRun;
+  const int g = bid / chunk, r = bid % chunk;
+  if (g >= n / chunk) return bid;
+  return g * chunk + (r % 8) * kRun + r / 8;
 }
+
+template <int V>
+struct Stage {
+  static constexpr int value = V;
+};
+
+constexpr int kKT = 64;           // keys per step
+constexpr int kIdxLds = 4096;     // selected-block list entries staged in LDS
 
 template <int BLK>
 __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const __bf16* __restrict__ Q,
                                                           const __bf16* __restrict__ K,
                                                           const __bf16* __restrict__ V,
                                                           __bf16* __restrict__ out) {
-  constexpr int NW = BLK / 32;  // waves
-  constexpr int NT = BLK / 32;  // 32-key subtiles per tile
-  __shared__ __attribute__((aligned(1024))) char smem[2 * BLK * 256 < 128 * 256 ? 128 * 256 : 2 * BLK * 256];
+  constexpr int NW = BLK / 32;     // waves = query groups
+  constexpr int NTH = 64 * NW;
+  constexpr int SPB = BLK / kKT;   // steps per key block (and per pooled tile)
+  constexpr int NT = kKT / 32;     // 32-key subtiles per step
+  constexpr int TB = kKT * 256;    // bytes of one K (or V) half
+  // Two stages (K and V halves) as four distinct LDS objects: the compiler then sees that reading
+  // one stage does not depend on the direct-to-LDS copies into the other.
+  __shared__ __attribute__((aligned(1024))) char sK0[TB];
+  __shared__ __attribute__((aligned(1024))) char sK1[TB];
+  __shared__ __attribute__((aligned(1024))) char sV0[TB];
+  __shared__ __attribute__((aligned(1024))) char sV1[TB];
   __shared__ uint32_t selm[kMaskWords];
-  char* Ks = smem;
-  char* Vs = smem + BLK * 256;
+  __shared__ uint16_t sidx[kIdxLds];
 
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  const int item = item_of(blockIdx.x, gridDim.x);
   const int h = item / dm.Nb, i = item % dm.Nb;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const uint32_t hh = lane >> 5, l32 = lane & 31, g16 = (lane >> 4) & 1, l16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS bases stay scalar
+  const uint32_t hh = lane >> 5, l32 = lane & 31;
   const int Nb = dm.Nb, B = dm.B, kk = dm.k;
   const int n_i = (i == Nb - 1) ? dm.n_last : B;
   const size_t head = (size_t)h * dm.L * 128;
+  const int32_t* sel = w.idx + ((size_t)h * Nb + i) * kk;
+  const bool do_tail = kk < Nb && (dm.phases & 2);
+  const bool do_first = do_tail && (dm.phases & 4);
+  const int nc = do_tail ? dm.Nbp / BLK : 0;
+  const __bf16* kl = reinterpret_cast<const __bf16*>(w.kbar_lo) + (size_t)h * dm.Nbp * 128;
+  const __bf16* vl = reinterpret_cast<const __bf16*>(w.vbar_lo) + (size_t)h * dm.Nbp * 128;
+  const __bf16* ht = reinterpret_cast<const __bf16*>(w.hbarT_lo) + (size_t)h * 128 * 128;
 
-  // Q^T operand: query row 32*wave + l32 of the block, d = 16 s + 8 hh .. +7
+  // selection: bit mask (pooled tiles) and the list (exact steps) in LDS
+  const int nmask = (dm.Nbp + 31) / 32;
+  for (int t = tid; t < nmask; t += NTH) selm[t] = 0u;
+  __syncthreads();
+  for (int t = tid; t < kk; t += NTH) {
+    const int j = sel[t];
+    if (t < kIdxLds) sidx[t] = (uint16_t)j;
+    atomicOr(&selm[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  auto block_of = [&](int t) -> int {  // t-th selected block (wave-uniform)
+    return __builtin_amdgcn_readfirstlane(kk <= kIdxLds ? (int)sidx[t] : sel[t]);
+  };
+
+  // Steps: exact (two per 128-row block; the ragged last block, which is last if selected, drops
+  // its second half when n_last <= 64), then pooled tiles, then the H-bar^T tile (128 rows over
+  // both arrays of a stage).
+  const int last_blk = block_of(kk - 1);
+  const int rows_last = last_blk == Nb - 1 ? dm.n_last : B;
+  const int E = (kk - 1) * SPB + (rows_last + kKT - 1) / kKT;  // exact steps
+  const bool ragged = (rows_last % kKT) != 0;                   // last exact step is partial
+  const int S_main = E + nc * SPB;
+  const int S_all = S_main + (do_first ? 1 : 0);
+
+  const uint32_t vb_row = copy_vbase<false>(wave, lane), vb_tr = copy_vbase<true>(wave, lane);
+  const uint32_t vb_row2 = copy_vbase<false>(wave, lane, 8), vb_tr2 = copy_vbase<true>(wave, lane, 8);
+  auto issue = [&](int s, auto stc) {
+    constexpr int ST = decltype(stc)::value;
+    char* Ks = ST ? sK1 : sK0;
+    char* Vs = ST ? sV1 : sV0;
+    if (s < E) {
+      const int j = block_of(s / SPB);
+      const int r0 = kKT * (s % SPB);
+      const int n_j = (j == Nb - 1) ? dm.n_last : B;
+      const size_t g0 = head + ((size_t)j * B + r0) * 128;
+      const uint32_t bytes = (uint32_t)(n_j - r0) * 256;  // rows past the block end read as zero
+      copy_tile<kKT, NW>(make_rsrc(K + g0, bytes), Ks, vb_row, wave, vb_row2);
+      copy_tile<kKT, NW>(make_rsrc(V + g0, bytes), Vs, vb_tr, wave, vb_tr2);
+    } else if (s < S_main) {
+      const size_t g0 = (size_t)(s - E) * kKT * 128;
+      copy_tile<kKT, NW>(make_rsrc(kl + g0, kKT * 256), Ks, vb_row, wave, vb_row2);
+      copy_tile<kKT, NW>(make_rsrc(vl + g0, kKT * 256), Vs, vb_tr, wave, vb_tr2);
+    } else {
+      copy_tile<kKT, NW>(make_rsrc(ht, kKT * 256), Ks, vb_row, wave, vb_row2);
+      copy_tile<kKT, NW>(make_rsrc(ht + kKT * 128, kKT * 256), Vs, vb_row, wave, vb_row2);
+    }
+  };
+  issue(0, Stage<0>{});
+
+  // Q^T operand: query row 32 wave + l32 of the block, d = 16 s + 8 hh .. +7
   bf16x8 qreg[8];
   {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head + (size_t)i * B * 128, n_i * 256);
     const uint32_t row = 32 * wave + l32;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, row * 256 + (16 * s + 8 * hh) * 2));
-  }
-
-  const int nmask = (dm.Nbp + 31) / 32;
-  for (int t = tid; t < nmask; t += BLK * 2) selm[t] = 0u;
-  __syncthreads();
-  const int32_t* sel = w.idx + ((size_t)h * Nb + i) * kk;
-  for (int t = tid; t < kk; t += BLK * 2) {
-    const int j = sel[t];
-    atomicOr(&selm[j >> 5], 1u << (j & 31));
+    for (int s = 0; s < 8; ++s)
+      qreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, row * 256 + (16 * s + 8 * hh) * 2));
   }
 
   const float cs = dm.scale * kLog2e;
+  const float lgB = __log2f((float)B), lgLast = __log2f((float)dm.n_last);
+  const float invB = 1.0f / (float)B, invLast = 1.0f / (float)dm.n_last;
   float m = -INFINITY, lsum = 0.f, beta = 0.f;
   f32x16 O[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) O[dt] = f32x16{};
-  f32x16 S[NT];
-  bf16x8 P[NT][2];
+  const LaneOffsets lofs = lane_offsets(lane);
 
-  // ---- phase 1: exact blocks --------------------------------------------------------------
-  for (int it = 0; it < kk; ++it) {
-    const int j = __builtin_amdgcn_readfirstlane(sel[it]);
-    const int n_j = (j == Nb - 1) ? dm.n_last : B;
-    const size_t r0 = head + (size_t)j * B * 128;
-    tile_to_lds<false>(make_rsrc(K + r0, n_j * 256), 256, Ks, BLK, wave, NW, lane);
-    tile_to_lds<true>(make_rsrc(V + r0, n_j * 256), 256, Vs, BLK, wave, NW, lane);
+  // One step s (ST = s & 1). KIND 0 = exact, 1 = exact partial (masked past valid rows), 2 = pooled.
+  auto step = [&](int s, auto stc, auto kc) {
+    constexpr int ST = decltype(stc)::value;
+    constexpr int KIND = decltype(kc)::value;
     wait_vmem();
-    __syncthreads();
-    qk_tile<NT>(Ks, qreg, S, l32, hh);
-    if (n_j < BLK) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const int key = 32 * t + 8 * (x >> 2) + 4 * hh + (x & 3);
-          if (key >= n_j) S[t][x] = -INFINITY;
-        }
-    }
+    __syncthreads();  // step s landed; step s - 1 no longer read by anyone
+    if (s + 1 < S_all) issue(s + 1, Stage<ST ^ 1>{});
+    f32x16 Sc[NT];
+    bf16x8 P[NT][2];
+    qk_tile<NT>(ST ? sK1 : sK0, 0, qreg, Sc, lofs);
     float mx = -INFINITY;
+    if constexpr (KIND == 2) {
+      const int key_base = (s - E) * kKT;  // pooled token index of the step's first key
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) mx = fmaxf(mx, S[t][x]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx * cs);
-    const float alpha = m == m_new ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
-    m = m_new;
-    lsum *= alpha;
-    beta *= alpha;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) O[dt] *= alpha;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(S[t][8 * u + e], cs, -m));
-          lsum += p;
-          P[t][u][e] = (__bf16)p;
-        }
-    pv_tile<NT>(Vs, P, O, hh, g16, l16);
-    __syncthreads();
-  }
-
-  const bool do_tail = kk < Nb && (dm.phases & 2);
-  // ---- phase 2: pooled tokens of the unselected blocks, zeroth order ---------------------------
-  if (do_tail) {
-    const float lgB = __log2f((float)B), lgLast = __log2f((float)dm.n_last);
-    const float invB = 1.0f / (float)B, invLast = 1.0f / (float)dm.n_last;
-    const __bf16* kl = reinterpret_cast<const __bf16*>(w.kbar_lo) + (size_t)h * dm.Nbp * 128;
-    const __bf16* vl = reinterpret_cast<const __bf16*>(w.vbar_lo) + (size_t)h * dm.Nbp * 128;
-    for (int c = 0; c < dm.Nbp / BLK; ++c) {
-      const size_t r0 = (size_t)c * BLK * 128;
-      tile_to_lds<false>(make_rsrc(kl + r0, BLK * 256), 256, Ks, BLK, wave, NW, lane);
-      tile_to_lds<true>(make_rsrc(vl + r0, BLK * 256), 256, Vs, BLK, wave, NW, lane);
-      wait_vmem();
-      __syncthreads();
-      qk_tile<NT>(Ks, qreg, S, l32, hh);
-      float mx = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const uint32_t word = selm[(c * BLK) / 32 + t];
+      for (int u = 0; u < NT; ++u) {
+        const uint32_t word = selm[(key_base + 32 * u) / 32];
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
           const int kin = 8 * (x >> 2) + 4 * hh + (x & 3);
-          const int j = c * BLK + 32 * t + kin;
+          const int j = key_base + 32 * u + kin;
           const bool ok = j < Nb && !((word >> kin) & 1u);
           const float lg = ok ? (j == Nb - 1 ? lgLast : lgB) : -INFINITY;
-          S[t][x] = fmaf(S[t][x], cs, lg);
-          mx = fmaxf(mx, S[t][x]);
+          Sc[u][x] = fmaf(Sc[u][x], cs, lg);
+          mx = fmaxf(mx, Sc[u][x]);
         }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);
-      const float alpha = m == m_new ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
+    } else {
+      if constexpr (KIND == 1) {
+        const int valid = rows_last - kKT * ((E - 1) % SPB);  // rows of the partial step
+#pragma unroll
+        for (int u = 0; u < NT; ++u)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) {
+            const int key = 32 * u + 8 * (x >> 2) + 4 * hh + (x & 3);
+            if (key >= valid) Sc[u][x] = -INFINITY;
+          }
+      }
+#pragma unroll
+      for (int u = 0; u < NT; ++u)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) mx = fmaxf(mx, Sc[u][x]);
+      mx *= cs;  // cs > 0: max of the scaled scores
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool up = mx > m + kLazy;
+    if (__builtin_expect(__ballot(up) != 0, 0)) {
+      const float m_new = up ? mx : m;
+      const float alpha = up ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;
       m = m_new;
       lsum *= alpha;
       beta *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) O[dt] *= alpha;
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int x = 8 * u + e;
-            const int j = c * BLK + 32 * t + 8 * (x >> 2) + 4 * hh + (x & 3);
-            const float p = __builtin_amdgcn_exp2f(S[t][x] - m);
-            lsum += p;
-            beta = fmaf(p, j == Nb - 1 ? invLast : invB, beta);
-            P[t][u][e] = (__bf16)p;
-          }
-      pv_tile<NT>(Vs, P, O, hh, g16, l16);
-      __syncthreads();
     }
-  }
-
-  // ---- phase 3: global first-order correction ------------------------------------------------
-  if (do_tail && (dm.phases & 4)) {
-    const __bf16* ht = reinterpret_cast<const __bf16*>(w.hbarT_lo) + (size_t)h * 128 * 128;
-    tile_to_lds<false>(make_rsrc(ht, 128 * 256), 256, smem, 128, wave, NW, lane);
-    wait_vmem();
-    __syncthreads();
-    f32x16 T[4];
-    qk_tile<4>(smem, qreg, T, l32, hh);
-    const float bt = (beta + __shfl_xor(beta, 32)) * dm.scale;
+    // a lane whose keys have all been masked so far still has m = -inf: its p must be 0, not NaN
+    const float mref = m == -INFINITY ? 0.0f : m;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) O[dt] += bt * T[dt];
-    __syncthreads();
+    for (int u = 0; u < NT; ++u)
+#pragma unroll
+      for (int v = 0; v < 2; ++v)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int x = 8 * v + e;
+          float p;
+          if constexpr (KIND == 2) {
+            const int j = (s - E) * kKT + 32 * u + 8 * (x >> 2) + 4 * hh + (x & 3);
+            p = __builtin_amdgcn_exp2f(Sc[u][x] - mref);
+            beta = fmaf(p, j == Nb - 1 ? invLast : invB, beta);
+          } else {
+            p = __builtin_amdgcn_exp2f(fmaf(Sc[u][x], cs, -mref));
+          }
+          lsum += p;
+          P[u][v][e] = (__bf16)p;
+        }
+    pv_tile<NT>(ST ? sV1 : sV0, 0, P, O, lofs);
+  };
+
+  const int E_full = E - (ragged ? 1 : 0);
+  int s0 = 0;
+  for (; s0 + 1 < E_full; s0 += 2) {
+    step(s0, Stage<0>{}, Stage<0>{});
+    step(s0 + 1, Stage<1>{}, Stage<0>{});
+  }
+  if (s0 < E_full) step(s0, Stage<0>{}, Stage<0>{});
+  if (ragged) {
+    if (E_full & 1)
+      step(E_full, Stage<1>{}, Stage<1>{});
+    else
+      step(E_full, Stage<0>{}, Stage<1>{});
+  }
+  for (int s = E; s < S_main; ++s) {
+    if (s & 1)
+      step(s, Stage<1>{}, Stage<2>{});
+    else
+      step(s, Stage<0>{}, Stage<2>{});
   }
 
-  // ---- epilogue ------------------------------------------------------------------------------
-  const float inv_l = 1.0f / (lsum + __shfl_xor(lsum, 32));
+  lsum += __shfl_xor(lsum, 32);
+  beta += __shfl_xor(beta, 32);
+  wait_vmem();
+  __syncthreads();  // every wave done with the last step; the H-bar^T tile (if any) has landed
+  const int hstage = S_main & 1;
+  // ---- phase 3: global first-order correction --------------------------------------------
+  if (do_first) {
+    f32x16 T2[2];
+    const float bt = beta * dm.scale;
+    qk_tile<2>(hstage ? sK1 : sK0, 0, qreg, T2, lofs);  // H-bar^T rows 0..63
+    O[0] += bt * T2[0];
+    O[1] += bt * T2[1];
+    qk_tile<2>(hstage ? sV1 : sV0, 0, qreg, T2, lofs);  // H-bar^T rows 64..127
+    O[2] += bt * T2[0];
+    O[3] += bt * T2[1];
+  }
+  // ---- epilogue: bf16 output rows via LDS (queries 0..63 in one array, 64..127 in the other) --
+  const int xs = do_first ? (hstage ^ 1) : 0;
+  char* stg_lo = xs ? sK1 : sK0;
+  char* stg_hi = xs ? sV1 : sV0;
+  const float inv_l = 1.0f / lsum;
   {
-    // O^T[dt] element x: query 32*wave + l32, column d = 32 dt + 8 (x/4) + 4 hh + (x%4)
     const uint32_t q = 32 * wave + l32;
+    char* stg = q < 64 ? stg_lo : stg_hi;
+    const uint32_t qr = q & 63;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -240,14 +342,16 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = (__bf16)(O[dt][4 * g + r] * inv_l);
         const uint32_t byte = (32 * dt + 8 * g + 4 * hh) * 2;
-        *reinterpret_cast<bf16x4*>(smem + q * 256 + swz_row(q, byte >> 4) * 16 + (byte & 15)) = v;
+        *reinterpret_cast<bf16x4*>(stg + qr * 256 + swz_row(qr, byte >> 4) * 16 + (byte & 15)) = v;
       }
   }
   __syncthreads();
   __bf16* orow = out + head + (size_t)i * B * 128;
-  for (int e = tid; e < n_i * 16; e += BLK * 2) {
+  for (int e = tid; e < n_i * 16; e += NTH) {
     const uint32_t q = e >> 4, c = e & 15;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(smem + q * 256 + swz_row(q, c) * 16);
+    const char* stg = q < 64 ? stg_lo : stg_hi;
+    const uint32_t qr = q & 63;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + qr * 256 + swz_row(qr, c) * 16);
     *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(orow) + q * 256 + c * 16) = v;
   }
 }

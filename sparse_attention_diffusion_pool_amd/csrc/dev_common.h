@@ -79,6 +79,45 @@ __device__ __forceinline__ void tile_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t s
   }
 }
 
+// Same with the row count and wave count known at compile time (fully unrolled).
+template <bool TR, int ROWS, int NWAVES>
+__device__ __forceinline__ void tile_to_lds_n(__amdgpu_buffer_rsrc_t r, char* lds, int wave, int lane) {
+  static_assert(ROWS % (4 * NWAVES) == 0, "tile rows must split evenly over the waves");
+#pragma unroll
+  for (int m = 0; m < ROWS / 4 / NWAVES; ++m) {
+    const int n = m * NWAVES + wave;
+    const uint32_t row = 4 * n + (lane >> 4);
+    const uint32_t pos = lane & 15;
+    const uint32_t src_chunk = TR ? swz_tr(row, pos) : swz_row(row, pos);
+    buf_load_lds16(r, lds + 1024 * n, row * 256 + src_chunk * 16);
+  }
+}
+
+// Direct copy of a ROWS x 256 B tile by NWAVES waves, with the per-lane part of the global
+// offset precomputed (vbase = copy_vbase<TR>(wave, lane)); instruction m of wave w covers tile
+// rows 4 (m NWAVES + w) .. +3. The swizzle only depends on (row & 15), which is the same for every
+// m when NWAVES is a multiple of 4, so one vbase serves all m (m NWAVES KB goes in soffset).
+// With NWAVES = 2, even and odd m differ by 8 in (row & 15): vbase2 is the offset for odd m.
+template <int ROWS, int NWAVES>
+__device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t vbase, int wave,
+                                          uint32_t vbase2 = 0) {
+  static_assert((NWAVES % 4 == 0 || NWAVES == 2) && ROWS % (4 * NWAVES) == 0, "copy_tile layout");
+#pragma unroll
+  for (int m = 0; m < ROWS / 4 / NWAVES; ++m)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + 1024 * (m * NWAVES + wave)), 16,
+                                             (NWAVES == 2 && (m & 1)) ? vbase2 : vbase,
+                                             (NWAVES == 2 ? (m & ~1) : m) * NWAVES * 1024, 0, 0);
+}
+
+// extra_rows: 0, or 8 for the odd instructions of a 2-wave copy
+template <bool TR>
+__device__ __forceinline__ uint32_t copy_vbase(int wave, int lane, int extra_rows = 0) {
+  const uint32_t row = 4 * wave + extra_rows + (lane >> 4);  // (row & 15) as in the instruction
+  const uint32_t pos = lane & 15;
+  const uint32_t chunk = TR ? swz_tr(row, pos) : swz_row(row, pos);
+  return row * 256 + chunk * 16;
+}
+
 // Address of a 16-byte row-read operand: row r, logical chunk c.
 __device__ __forceinline__ const char* row_addr(const char* tile, uint32_t r, uint32_t c) {
   return tile + r * 256 + swz_row(r, c) * 16;
