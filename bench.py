@@ -88,6 +88,65 @@ def cpu_baseline(w, heads, sample_note):
             "sample": sample_note, "seconds": secs, "cpu": platform.processor() or platform.machine()}
 
 
+KERNELS = ("stats_pass_bf16", "stats_cov_bf16", "stats_finalize", "stats_f32", "route_kernel", "attend_bf16",
+           "attend_f32", "copyBuffer", "Fill")
+
+
+def short_kernel(name: str) -> str:
+    return next((k for k in KERNELS if k in name), name[:48])
+
+
+def summarize_trace(d: str) -> None:
+    """Markdown table from a rocprofv3 --kernel-trace --stats --output-format csv directory."""
+    import csv
+    path = next(os.path.join(r, f) for r, _, fs in os.walk(d) for f in fs if f.endswith("kernel_stats.csv"))
+    rows = list(csv.DictReader(open(path)))
+    print("| kernel | calls | average (us) | min (us) | max (us) | share |")
+    print("|---|---|---|---|---|---|")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        print(f"| {short_kernel(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+              f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+
+
+def summarize_traffic(d: str, command: str) -> None:
+    """HBM-side bytes per attention launch from two rocprofv3 --pmc passes (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch) over the benchmark, each scaled by what the same counter reads for
+    a 1 GiB device copy (bench.py --copy-calibration). Writes the traffic record the benchmark
+    reports (valid while the attention kernel's sources are unchanged) and prints a summary."""
+    import collections
+    import csv
+
+    def per_kernel(sub, counter):
+        agg = collections.defaultdict(float)
+        for r in csv.DictReader(open(os.path.join(d, sub, "run_counter_collection.csv"))):
+            if r["Counter_Name"] == counter:
+                agg[(int(r["Dispatch_Id"]), short_kernel(r["Kernel_Name"]))] += float(r["Counter_Value"])
+        per = collections.defaultdict(list)
+        for (_, k), v in agg.items():
+            per[k].append(v * 1024.0)
+        return {k: sum(v) / len(v) for k, v in per.items()}
+
+    fetch, write = per_kernel("fetch", "FETCH_SIZE"), per_kernel("write", "WRITE_SIZE")
+    cal = 1 << 30
+    f_scale = cal / per_kernel("copy_fetch", "FETCH_SIZE")["copyBuffer"]
+    w_scale = cal / per_kernel("copy_write", "WRITE_SIZE")["copyBuffer"]
+    rec = {"kernel": "attend_bf16", "workload": "wan720p-like-L75600", "source_sha": source_sha(ATTEND_SRC),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "fetch_bytes_per_launch": fetch["attend_bf16"] * f_scale,
+           "write_bytes_per_launch": write["attend_bf16"] * w_scale,
+           "command": command}
+    rec["hbm_bytes_per_launch"] = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(f"copy calibration (1 GiB device copy): FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f}\n")
+    print("| kernel | fetched GB per launch (scaled) | written GB per launch (scaled) |")
+    print("|---|---|---|")
+    for k in sorted(fetch, key=lambda k: -fetch[k]):
+        if k in ("copyBuffer", "Fill"):
+            continue
+        print(f"| {k} | {fetch[k] * f_scale / 1e9:.3f} | {write.get(k, 0.0) * w_scale / 1e9:.3f} |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,11 +155,24 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="index into workloads.CONFIGS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quality", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=2)
+    ap.add_argument("--cpu-heads", type=int, default=5)
     ap.add_argument("--phases", type=int, default=7)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (scales the HBM byte counters)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a markdown summary of a rocprofv3 --stats csv output directory and exit")
+    ap.add_argument("--summarize-traffic", metavar="DIR",
+                    help="turn the fetch/write/copy_fetch/copy_write --pmc csv directories under DIR into "
+                         "the attention kernel's traffic record and exit")
+    ap.add_argument("--traffic-command", default="", help="command line recorded with --summarize-traffic")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic, args.traffic_command)
+        return
 
     if args.copy_calibration:
         import torch

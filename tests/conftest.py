@@ -28,3 +28,11 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+# A planted oracle mistake for tests/test_oracle_mutations.py (set only in its subprocesses).
+if os.environ.get("PISA_ORACLE_MUTANT"):
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import oracle_mutants
+
+    oracle_mutants.apply(os.environ["PISA_ORACLE_MUTANT"])
