@@ -31,7 +31,7 @@ struct Work {
   float* qbar;      // [H][Nb][d]   pooled scaled queries (mean of scale*q over the block)
   float* kbar;      // [H][Nb][d]   key centroids
   float* vsum;      // [H][Nb][d]   value sums
-  float* G;         // [H][NC][d][d] partial sums of K_j^T V_j
+  float* G;         // [H][NC][d][d] partial sums of H_j = K_j^T V_j - kbar_j (sum V_j)^T
   float* hbar;      // [H][d][d]    H-bar
   float* M;         // [H][Nb]      ||H_j - H-bar||_F
   void* kbar_lo;    // bf16 [H][Nbp][d] centroids, zero rows past Nb      (bf16 path only)

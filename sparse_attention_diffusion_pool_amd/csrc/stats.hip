@@ -5,10 +5,10 @@
 // M_j = ||H_j - H-bar||).
 //
 // Pass A (one workgroup per 16 consecutive blocks of a head): column sums of Q, K, V per block
-// (pooled scaled query, key centroid, value sum) and the partial sum of K_j^T V_j over its
-// blocks. Finalize (per head): H-bar = (sum_j K_j^T V_j - sum_j kbar_j (sum V_j)^T) / N_b, using
-// H_j = K_j^T V_j - n_j kbar_j vbar_j^T; bf16 copies of the pooled tokens and of H-bar^T for the
-// attention kernel. Covariance pass (one workgroup per block): H_j again, then
+// (pooled scaled query, key centroid, value sum) and the partial sum of the block first-order
+// matrices over its blocks, H_j = K_j^T V_j - kbar_j (sum V_j)^T (= sum_n (k_n - kbar_j)^T v_n).
+// Finalize (per head): H-bar = (sum of the partials) / N_b; bf16 copies of the pooled tokens and
+// of H-bar^T for the attention kernel. Covariance pass (one workgroup per block): H_j again, then
 // M_j = ||H_j - H-bar||_F.
 //
 // bf16 inputs: K_j^T V_j on v_mfma_f32_32x32x16_bf16 (products of bf16 values are exact in fp32,
@@ -44,75 +44,124 @@ __device__ __forceinline__ void ktv_mfma(const char* Ks, const char* Vs, f32x16 
   }
 }
 
+template <int V>
+struct Stage {
+  static constexpr int value = V;
+};
+
+// Pass A, bf16. The K and V tiles of block j + 1 are copied to LDS (and its Q rows loaded into
+// registers) while block j is summed and multiplied, through two LDS stages held as distinct
+// objects. The chunk's partial is written already corrected by the centroids:
+// G_c = sum_{j in c} (K_j^T V_j - kbar_j (sum V_j)^T) = sum_{j in c} H_j.
 template <int BLK>
 __global__ __launch_bounds__(256) void stats_pass_bf16(Dims dm, Work w, const __bf16* __restrict__ Q,
                                                        const __bf16* __restrict__ K,
                                                        const __bf16* __restrict__ V) {
-  __shared__ __attribute__((aligned(1024))) char Ks[BLK * 256];
-  __shared__ __attribute__((aligned(1024))) char Vs[BLK * 256];
+  __shared__ __attribute__((aligned(1024))) char Ks0[BLK * 256];
+  __shared__ __attribute__((aligned(1024))) char Vs0[BLK * 256];
+  __shared__ __attribute__((aligned(1024))) char Ks1[BLK * 256];
+  __shared__ __attribute__((aligned(1024))) char Vs1[BLK * 256];
   __shared__ float red[4][3][128];
+  __shared__ float skb[kStatsChunk][128];  // centroids and value sums of the chunk's blocks
+  __shared__ float svs[kStatsChunk][128];
+  constexpr int QR = BLK / 16;  // Q rows (16-byte pieces) per thread
   const int h = blockIdx.y, c = blockIdx.x;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j0 = c * kStatsChunk, j1 = min(dm.Nb, j0 + kStatsChunk);
   const size_t head = (size_t)h * dm.L * 128;
   f32x16 acc[4];
   for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x16{};
   const int p = tid & 15, rg = tid >> 4;  // column chunk (8 columns) and row group for the sums
+  u32x4 qa[QR], qb[QR];
 
-  for (int j = j0; j < j1; ++j) {
-    const int n = (j == dm.Nb - 1) ? dm.n_last : dm.B;
+  auto rows_of = [&](int j) { return (j == dm.Nb - 1) ? dm.n_last : dm.B; };
+  auto issue = [&](int j, auto stc, u32x4* qr) {
+    constexpr int ST = decltype(stc)::value;
+    const int n = rows_of(j);
     const size_t r0 = head + (size_t)j * dm.B * 128;
-    __amdgpu_buffer_rsrc_t rk = make_rsrc(K + r0, n * 256);
-    __amdgpu_buffer_rsrc_t rv = make_rsrc(V + r0, n * 256);
-    __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + r0, n * 256);
-    tile_to_lds<true>(rk, 256, Ks, BLK, wave, 4, lane);
-    tile_to_lds<true>(rv, 256, Vs, BLK, wave, 4, lane);
+    tile_to_lds<true>(make_rsrc(K + r0, n * 256), 256, ST ? Ks1 : Ks0, BLK, wave, 4, lane);
+    tile_to_lds<true>(make_rsrc(V + r0, n * 256), 256, ST ? Vs1 : Vs0, BLK, wave, 4, lane);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + r0, n * 256);
+#pragma unroll
+    for (int e = 0; e < QR; ++e) qr[e] = buf_load16(rq, (rg + 16 * e) * 256 + p * 16);
+  };
+
+  auto block = [&](int j, auto stc, const u32x4* qr) {
+    constexpr int ST = decltype(stc)::value;
+    const char* Ks = ST ? Ks1 : Ks0;
+    const char* Vs = ST ? Vs1 : Vs0;
+    const int n = rows_of(j);
     float qs[8] = {0, 0, 0, 0, 0, 0, 0, 0}, ks8[8] = {0, 0, 0, 0, 0, 0, 0, 0}, vs8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int r = rg; r < BLK; r += 16) {
+#pragma unroll
+    for (int e = 0; e < QR; ++e) {
       float f[8];
-      unpack_bf16x8(buf_load16(rq, r * 256 + p * 16), f);
-      for (int e = 0; e < 8; ++e) qs[e] += f[e];
+      unpack_bf16x8(qr[e], f);
+      for (int x = 0; x < 8; ++x) qs[x] += f[x];
     }
-    wait_vmem();
-    __syncthreads();
     for (int r = rg; r < BLK; r += 16) {
       float f[8];
       unpack_bf16x8(*reinterpret_cast<const u32x4*>(Ks + r * 256 + swz_tr(r, p) * 16), f);
-      for (int e = 0; e < 8; ++e) ks8[e] += f[e];
+      for (int x = 0; x < 8; ++x) ks8[x] += f[x];
       unpack_bf16x8(*reinterpret_cast<const u32x4*>(Vs + r * 256 + swz_tr(r, p) * 16), f);
-      for (int e = 0; e < 8; ++e) vs8[e] += f[e];
+      for (int x = 0; x < 8; ++x) vs8[x] += f[x];
     }
-    for (int e = 0; e < 8; ++e) {
-      qs[e] += __shfl_xor(qs[e], 16);
-      qs[e] += __shfl_xor(qs[e], 32);
-      ks8[e] += __shfl_xor(ks8[e], 16);
-      ks8[e] += __shfl_xor(ks8[e], 32);
-      vs8[e] += __shfl_xor(vs8[e], 16);
-      vs8[e] += __shfl_xor(vs8[e], 32);
+    for (int x = 0; x < 8; ++x) {
+      qs[x] += __shfl_xor(qs[x], 16);
+      qs[x] += __shfl_xor(qs[x], 32);
+      ks8[x] += __shfl_xor(ks8[x], 16);
+      ks8[x] += __shfl_xor(ks8[x], 32);
+      vs8[x] += __shfl_xor(vs8[x], 16);
+      vs8[x] += __shfl_xor(vs8[x], 32);
     }
     if (lane < 16) {
-      for (int e = 0; e < 8; ++e) {
-        red[wave][0][8 * p + e] = qs[e];
-        red[wave][1][8 * p + e] = ks8[e];
-        red[wave][2][8 * p + e] = vs8[e];
+      for (int x = 0; x < 8; ++x) {
+        red[wave][0][8 * p + x] = qs[x];
+        red[wave][1][8 * p + x] = ks8[x];
+        red[wave][2][8 * p + x] = vs8[x];
       }
     }
     ktv_mfma<BLK>(Ks, Vs, acc, wave, lane);
-    __syncthreads();
+    __syncthreads();  // red complete
     if (tid < 128) {
       const float inv = 1.0f / (float)n;
-      float sq = red[0][0][tid] + red[1][0][tid] + red[2][0][tid] + red[3][0][tid];
-      float sk = red[0][1][tid] + red[1][1][tid] + red[2][1][tid] + red[3][1][tid];
-      float sv = red[0][2][tid] + red[1][2][tid] + red[2][2][tid] + red[3][2][tid];
+      const float sq = red[0][0][tid] + red[1][0][tid] + red[2][0][tid] + red[3][0][tid];
+      const float sk = red[0][1][tid] + red[1][1][tid] + red[2][1][tid] + red[3][1][tid];
+      const float sv = red[0][2][tid] + red[1][2][tid] + red[2][2][tid] + red[3][2][tid];
       const size_t o = ((size_t)h * dm.Nb + j) * 128 + tid;
       w.qbar[o] = sq * dm.scale * inv;
       w.kbar[o] = sk * inv;
       w.vsum[o] = sv;
+      skb[j - j0][tid] = sk * inv;
+      svs[j - j0][tid] = sv;
+    }
+  };
+
+  issue(j0, Stage<0>{}, qa);
+  for (int j = j0; j < j1; j += 2) {
+    wait_vmem();
+    __syncthreads();  // stage 0 landed; stage 1 and red free
+    if (j + 1 < j1) issue(j + 1, Stage<1>{}, qb);
+    block(j, Stage<0>{}, qa);
+    if (j + 1 < j1) {
+      wait_vmem();
+      __syncthreads();
+      if (j + 2 < j1) issue(j + 2, Stage<0>{}, qa);
+      block(j + 1, Stage<1>{}, qb);
     }
   }
-  // partial sum of K_j^T V_j over this chunk: G[h][c][a][b]
+  __syncthreads();  // skb / svs complete
+  // G[h][c][a][b] = acc - sum_j kbar_j[a] vsum_j[b]
   float* G = w.G + ((size_t)h * dm.NC + c) * 128 * 128;
   const int hh = lane >> 5, l32 = lane & 31;
+  for (int jj = 0; jj < j1 - j0; ++jj) {
+    float vb[4];
+    for (int ct = 0; ct < 4; ++ct) vb[ct] = svs[jj][32 * ct + l32];
+    for (int x = 0; x < 16; ++x) {
+      const float ka = skb[jj][32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3)];
+      for (int ct = 0; ct < 4; ++ct) acc[ct][x] = fmaf(-ka, vb[ct], acc[ct][x]);
+    }
+  }
   for (int ct = 0; ct < 4; ++ct)
     for (int x = 0; x < 16; ++x) {
       const int a = 32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3);
@@ -169,6 +218,7 @@ __global__ __launch_bounds__(256) void stats_f32(Dims dm, Work w, const float* _
   __shared__ float Ks[SUB][D + 4];
   __shared__ float Vs[SUB][D + 4];
   __shared__ float red[256 / 64];
+  __shared__ float ckb[D], cvs[D];  // centroid and value sum of the current block (pass A)
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
   const int a0 = P * (tid / 16), b0 = P * (tid % 16);
@@ -189,6 +239,7 @@ __global__ __launch_bounds__(256) void stats_f32(Dims dm, Work w, const float* _
     if (COV)
       for (int x = 0; x < P; ++x)
         for (int y = 0; y < P; ++y) acc[x][y] = 0.f;
+    if (!COV) __syncthreads();  // every thread done with the previous block's ckb / cvs
     if (!COV && tid < D) {
       float sq = 0.f, sk = 0.f, sv = 0.f;
       for (int r = 0; r < n; ++r) {
@@ -200,6 +251,8 @@ __global__ __launch_bounds__(256) void stats_f32(Dims dm, Work w, const float* _
       w.qbar[o] = sq * dm.scale / (float)n;
       w.kbar[o] = sk / (float)n;
       w.vsum[o] = sv;
+      ckb[tid] = sk / (float)n;
+      cvs[tid] = sv;
     }
     for (int s0 = 0; s0 < n; s0 += SUB) {
       __syncthreads();
@@ -215,6 +268,10 @@ __global__ __launch_bounds__(256) void stats_f32(Dims dm, Work w, const float* _
           const float kv = Ks[r][a0 + x];
           for (int y = 0; y < P; ++y) acc[x][y] += kv * Vs[r][b0 + y];
         }
+    }
+    if (!COV) {  // the chunk partial sums H_j = K_j^T V_j - kbar_j (sum V_j)^T
+      for (int x = 0; x < P; ++x)
+        for (int y = 0; y < P; ++y) acc[x][y] = fmaf(-ckb[a0 + x], cvs[b0 + y], acc[x][y]);
     }
     if (COV) {
       const float* kb = w.kbar + ((size_t)h * dm.Nb + j) * D;
@@ -240,42 +297,36 @@ __global__ __launch_bounds__(256) void stats_f32(Dims dm, Work w, const float* _
 }
 
 // ---------------------------------------------------------------------------------------------
-// Finalize: H-bar, and (bf16 path) bf16 pooled tokens and H-bar^T.
-// Grid (16, H): workgroup x owns rows 8x..8x+7 of H-bar for d = 128 (4x..4x+3 for d = 64) and
-// converts the pooled rows j = x, x + 16, ...
+// Finalize: H-bar = (sum_c G_c) / N_b (the partials already hold sum_{j in c} H_j), and (bf16 path)
+// bf16 pooled tokens and H-bar^T. Grid (D * D / 256, H): one H-bar entry per thread; pooled rows
+// are spread over the same grid.
 // ---------------------------------------------------------------------------------------------
 
 template <int D>
 __global__ __launch_bounds__(256) void stats_finalize(Dims dm, Work w) {
-  constexpr int E = D * D / 16 / 256;  // entries per thread
   const int h = blockIdx.y, x = blockIdx.x, tid = threadIdx.x;
-  const float* kb = w.kbar + (size_t)h * dm.Nb * D;
-  const float* vs = w.vsum + (size_t)h * dm.Nb * D;
-  const float* G = w.G + (size_t)h * dm.NC * D * D;
-  const int a_base = x * (D / 16);
-  int a[E], b[E];
-  float g[E], corr[E];
-  for (int e = 0; e < E; ++e) {
-    const int lin = tid + 256 * e;
-    a[e] = a_base + lin / D;
-    b[e] = lin % D;
-    g[e] = 0.f;
-    corr[e] = 0.f;
+  const int e = x * 256 + tid;  // entry a * D + b
+  const int a = e / D, b = e % D;
+  const float* G = w.G + (size_t)h * dm.NC * D * D + e;
+  float g0 = 0.f, g1 = 0.f, g2 = 0.f, g3 = 0.f;
+  int c = 0;
+  for (; c + 4 <= dm.NC; c += 4) {
+    g0 += G[(size_t)c * D * D];
+    g1 += G[(size_t)(c + 1) * D * D];
+    g2 += G[(size_t)(c + 2) * D * D];
+    g3 += G[(size_t)(c + 3) * D * D];
   }
-  for (int c = 0; c < dm.NC; ++c)
-    for (int e = 0; e < E; ++e) g[e] += G[(size_t)c * D * D + a[e] * D + b[e]];
-  for (int j = 0; j < dm.Nb; ++j)
-    for (int e = 0; e < E; ++e) corr[e] += kb[(size_t)j * D + a[e]] * vs[(size_t)j * D + b[e]];
-  const float inv_nb = 1.0f / (float)dm.Nb;
-  for (int e = 0; e < E; ++e) {
-    const float v = (g[e] - corr[e]) * inv_nb;
-    w.hbar[(size_t)h * D * D + a[e] * D + b[e]] = v;
-    if (dm.dtype == 0) reinterpret_cast<__bf16*>(w.hbarT_lo)[(size_t)h * D * D + b[e] * D + a[e]] = (__bf16)v;
-  }
+  for (; c < dm.NC; ++c) g0 += G[(size_t)c * D * D];
+  const float v = ((g0 + g1) + (g2 + g3)) / (float)dm.Nb;
+  w.hbar[(size_t)h * D * D + e] = v;
   if (dm.dtype == 0) {
+    reinterpret_cast<__bf16*>(w.hbarT_lo)[(size_t)h * D * D + b * D + a] = (__bf16)v;
+    const float* kb = w.kbar + (size_t)h * dm.Nb * D;
+    const float* vs = w.vsum + (size_t)h * dm.Nb * D;
     __bf16* kl = reinterpret_cast<__bf16*>(w.kbar_lo) + (size_t)h * dm.Nbp * D;
     __bf16* vl = reinterpret_cast<__bf16*>(w.vbar_lo) + (size_t)h * dm.Nbp * D;
-    for (int j = x + 16 * (tid / D); j < dm.Nbp; j += 16 * (256 / D)) {
+    const int per = 256 / D;  // pooled rows per workgroup pass
+    for (int j = x * per + tid / D; j < dm.Nbp; j += gridDim.x * per) {
       const int cc = tid % D;
       float kv = 0.f, vv = 0.f;
       if (j < dm.Nb) {
@@ -340,7 +391,7 @@ hipError_t launch_stats_cov_f32(const Dims& dm, const Work& w, const void* K, co
 }
 
 hipError_t launch_stats_finalize(const Dims& dm, const Work& w, hipStream_t s) {
-  dim3 grid(16, dm.H);
+  dim3 grid(dm.d * dm.d / 256, dm.H);
   if (dm.d == 128)
     hipLaunchKernelGGL(stats_finalize<128>, grid, dim3(256), 0, s, dm, w);
   else
