@@ -147,6 +147,143 @@ def summarize_traffic(d: str, command: str) -> None:
         print(f"| {k} | {fetch[k] * f_scale / 1e9:.3f} | {write.get(k, 0.0) * w_scale / 1e9:.3f} |")
 
 
+def time_stages(plan, qd, kd, vd, out, stream, steps, warmup):
+    """Per-step stage times (ms) of `steps` forwards after `warmup` untimed ones, HIP events on the
+    library's stream: arrays stats, route, attend, step, plus the span of all timed steps."""
+    import torch
+    for _ in range(warmup):
+        plan.forward(qd, kd, vd, out, stream)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    wall0 = time.perf_counter()
+    for s in range(steps):
+        ev[s][0].record(stream)
+        plan.forward_stats(qd, kd, vd, stream)
+        ev[s][1].record(stream)
+        plan.forward_route(stream)
+        ev[s][2].record(stream)
+        plan.forward_attend(qd, kd, vd, out, stream)
+        ev[s][3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    t = {name: np.array([ev[s][a].elapsed_time(ev[s][b]) for s in range(steps)])
+         for name, a, b in (("stats", 0, 1), ("route", 1, 2), ("attend", 2, 3), ("step", 0, 3))}
+    t["span"] = ev[0][0].elapsed_time(ev[steps - 1][3])
+    t["wall_ms"] = wall * 1e3
+    return t
+
+
+def selection_of(plan, info, H, dev):
+    import torch
+    idx = torch.empty((H, info["n_blocks"], info["k"]), dtype=torch.int32, device=dev)
+    plan.debug_copy_selection(idx)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy()
+
+
+# (label, keep override (None = the workload's), phase mask): the method, its zeroth-order-only
+# ablation, keep-or-drop block-sparse attention at the same k, and dense attention (every block
+# exact) through the same kernel
+MODES = (("pisa", None, 7), ("zeroth-order only", None, 3), ("keep-or-drop", None, 1), ("dense", 1.0, 1))
+
+
+def compare_modes(w, steps, warmup, quality_blocks=8):
+    """One workload under every mode: time per forward, executed TFLOP/s, speed-up over dense
+    through the same kernel, and relative L2 error against fp64 dense attention on sampled query
+    blocks of the first and last head. Prints a markdown table and returns the records."""
+    import torch
+    from sparse_attention_diffusion_pool_amd import _lib as L
+    from workloads import layer_inputs
+    q, k, v = layer_inputs(w)
+    dev = torch.device("cuda", 0)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    stream = torch.cuda.current_stream()
+    dtype = L.DTYPE_BF16 if w.dtype == "bf16" else L.DTYPE_F32
+    rng = np.random.default_rng(0)
+    nb = -(-w.L // w.B)
+    samples = [(h, int(i)) for h in (0, w.H - 1) for i in sorted(rng.choice(nb, size=min(quality_blocks, nb),
+                                                                            replace=False))]
+    refs = {}
+    recs = []
+    for label, keep, phases in MODES:
+        kp = w.keep if keep is None else keep
+        plan = L.Plan(w.L, w.H, w.d, w.B, kp, dtype=dtype, phases=phases)
+        plan.attach_workspace(device=dev)
+        info = plan.info()
+        out = torch.empty_like(qd)
+        t = time_stages(plan, qd, kd, vd, out, stream, steps, warmup)
+        fl = algorithmic_flops(selection_of(plan, info, w.H, dev), w.L, w.d, w.B, phases)
+        num = den = 0.0
+        for h, i in samples:
+            rows = np.arange(i * w.B, min(w.L, (i + 1) * w.B))
+            if (h, i) not in refs:
+                refs[(h, i)] = dense_rows(q[h], k[h], v[h], rows, info["scale"])
+            ref = refs[(h, i)]
+            got = out[h, rows[0]:rows[-1] + 1].to(torch.float64).cpu()
+            num += float(((got - ref) ** 2).sum())
+            den += float((ref ** 2).sum())
+        ms = t["span"] / steps
+        recs.append({"mode": label, "keep": kp, "k": info["k"], "phases": phases, "ms_per_call": ms,
+                     "attend_ms": float(t["attend"].mean()), "stats_ms": float(t["stats"].mean()),
+                     "route_ms": float(t["route"].mean()), "executed_flops": fl["total"],
+                     "tflops": fl["total"] / (ms * 1e-3) / 1e12, "rel_l2_vs_dense": math.sqrt(num / den)})
+        plan.destroy()
+        del out
+        torch.cuda.empty_cache()
+    dense_ms = recs[-1]["ms_per_call"]
+    print(f"workload {w.name} (H={w.H}, L={w.L}, d={w.d}, B={w.B}, {w.dtype}); {steps} timed calls after "
+          f"{warmup} warm-up; quality: {len(samples)} query blocks of heads 0 and {w.H - 1} against fp64 dense\n")
+    print("| mode | keep | k | ms per call | attention ms | executed TFLOP/s | speed-up vs dense | rel-L2 vs dense |")
+    print("|---|---|---|---|---|---|---|---|")
+    for r in recs:
+        print(f"| {r['mode']} | {r['keep']:g} | {r['k']} | {r['ms_per_call']:.3f} | {r['attend_ms']:.3f} | "
+              f"{r['tflops']:.1f} | {dense_ms / r['ms_per_call']:.2f}x | {r['rel_l2_vs_dense']:.4f} |")
+    return recs
+
+
+SWEEP_GRIDS = ((4, 32, 32), (8, 32, 32), (16, 32, 32), (32, 32, 32))   # L = 4K, 8K, 16K, 32K
+SWEEP_KEEP = (0.05, 0.1, 0.125, 0.2, 0.3, 0.5)
+
+
+def latency_sweep(H, steps, warmup):
+    """Forward latency of the method over sequence length and density (bf16, d = 128, B = 128,
+    H heads, video-like token grids), against dense attention through the same kernel."""
+    import torch
+    from sparse_attention_diffusion_pool_amd import _lib as L
+    from workloads import custom, layer_inputs
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    rows = []
+    for grid in SWEEP_GRIDS:
+        w = custom(f"sweep-{'x'.join(map(str, grid))}", H, grid, 128, 128, 0.1, "bf16")
+        q, k, v = layer_inputs(w)
+        qd, kd, vd = (t.to(dev) for t in (q, k, v))
+        out = torch.empty_like(qd)
+        res = {}
+        for keep in SWEEP_KEEP + (1.0,):
+            plan = L.Plan(w.L, H, 128, 128, keep, dtype=L.DTYPE_BF16, phases=1 if keep == 1.0 else 7)
+            plan.attach_workspace(device=dev)
+            t = time_stages(plan, qd, kd, vd, out, stream, steps, warmup)
+            res[keep] = (t["span"] / steps, plan.info()["k"], float(t["attend"].mean()))
+            plan.destroy()
+        rows.append((w.L, res))
+        print(f"[sweep] L={w.L}: " + " ".join(f"{kp:g}:{r[0]:.3f}ms" for kp, r in res.items()),
+              file=sys.stderr, flush=True)
+        del qd, kd, vd, out
+        torch.cuda.empty_cache()
+    print(f"bf16, H={H}, d=128, B=128, batch 1, video-like grids (T x 32 x 32); ms per forward "
+          f"(statistics + routing + attention), mean of {steps} calls after {warmup} warm-up; in brackets "
+          f"the speed-up over dense attention through the same kernel (keep = 1; attention stage only, since "
+          f"dense attention needs no statistics or routing)\n")
+    print("| L | dense ms | " + " | ".join(f"keep {kp:g}" for kp in SWEEP_KEEP) + " |")
+    print("|---|---|" + "---|" * len(SWEEP_KEEP))
+    for Lx, res in rows:
+        dense = res[1.0][2]
+        print(f"| {Lx} | {dense:.3f} | " + " | ".join(f"{res[kp][0]:.3f} ({dense / res[kp][0]:.2f}x, k={res[kp][1]})"
+                                                     for kp in SWEEP_KEEP) + " |")
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +302,12 @@ def main():
                     help="turn the fetch/write/copy_fetch/copy_write --pmc csv directories under DIR into "
                          "the attention kernel's traffic record and exit")
     ap.add_argument("--traffic-command", default="", help="command line recorded with --summarize-traffic")
+    ap.add_argument("--modes", action="store_true",
+                    help="compare the method, its zeroth-order-only ablation, keep-or-drop and dense attention "
+                         "on the workload (markdown table) and exit")
+    ap.add_argument("--sweep", action="store_true",
+                    help="latency over L = 4K..32K and keep 0.05..0.5 against dense (markdown table) and exit")
+    ap.add_argument("--sweep-heads", type=int, default=24)
     args = ap.parse_args()
 
     if args.summarize_trace:
@@ -190,6 +333,14 @@ def main():
               "path (heads would shard across GPUs with no exchange); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    if args.modes:
+        from workloads import CONFIGS
+        compare_modes(CONFIGS[args.workload], args.steps, args.warmup)
+        return
+    if args.sweep:
+        latency_sweep(args.sweep_heads, args.steps, args.warmup)
+        return
+
     import torch
     from sparse_attention_diffusion_pool_amd import _lib as L
     from workloads import CONFIGS, layer_inputs
@@ -208,36 +359,12 @@ def main():
     stream = torch.cuda.current_stream()
     print(f"[bench] {w.name}: generated in {t_gen:.1f}s; N_b={info['n_blocks']} k={info['k']}", file=sys.stderr, flush=True)
 
-    for _ in range(args.warmup):
-        plan.forward(qd, kd, vd, out, stream)
-    torch.cuda.synchronize()
-
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for s in range(K):
-        ev[s][0].record(stream)
-        plan.forward_stats(qd, kd, vd, stream)
-        ev[s][1].record(stream)
-        plan.forward_route(stream)
-        ev[s][2].record(stream)
-        plan.forward_attend(qd, kd, vd, out, stream)
-        ev[s][3].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
+    t = time_stages(plan, qd, kd, vd, out, stream, K, args.warmup)
+    step_ms, stats_ms, route_ms, attend_ms = t["step"], t["stats"], t["route"], t["attend"]
+    ms_per_step = t["span"] / K
 
-    step_ms = np.array([ev[s][0].elapsed_time(ev[s][3]) for s in range(K)])
-    stats_ms = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in range(K)])
-    route_ms = np.array([ev[s][1].elapsed_time(ev[s][2]) for s in range(K)])
-    attend_ms = np.array([ev[s][2].elapsed_time(ev[s][3]) for s in range(K)])
-    span_ms = ev[0][0].elapsed_time(ev[K - 1][3])
-    ms_per_step = span_ms / K
-
-    idx = torch.empty((w.H, info["n_blocks"], info["k"]), dtype=torch.int32, device=dev)
-    plan.debug_copy_selection(idx, stream)
-    torch.cuda.synchronize()
-    fl = algorithmic_flops(idx.cpu().numpy(), w.L, w.d, w.B, args.phases)
+    fl = algorithmic_flops(selection_of(plan, info, w.H, dev), w.L, w.d, w.B, args.phases)
     tflops = fl["total"] / (ms_per_step * 1e-3) / 1e12
     attend_tflops = fl["attend"] / (attend_ms.mean() * 1e-3) / 1e12
     stats_gbps = info["bytes_stats"] / (stats_ms.mean() * 1e-3) / 1e9
@@ -267,7 +394,8 @@ def main():
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "ms": {"step_median": round(float(np.median(step_ms)), 4), "step_min": round(float(step_ms.min()), 4),
                "stats": round(float(stats_ms.mean()), 4), "route": round(float(route_ms.mean()), 4),
-               "attend": round(float(attend_ms.mean()), 4), "wall_per_step": round(wall / K * 1e3, 4)},
+               "attend": round(float(attend_ms.mean()), 4),
+               "wall_per_step": round(t["wall_ms"] / K, 4)},
         "executed_flops": fl,
         "stats_hbm": {"bytes": info["bytes_stats"], "GBps": round(stats_gbps, 1),
                       "frac": round(stats_gbps / PEAK_HBM_GBPS, 4)},
