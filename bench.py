@@ -43,10 +43,11 @@ def source_sha(path: str) -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_flops(idx: np.ndarray, L: int, d: int, B: int, phases: int) -> dict:
+def algorithmic_flops(idx: np.ndarray, L: int, d: int, B: int, phases: int, first_order: int = 0) -> dict:
     """Executed FLOPs of one call from the actual selection idx [H, N_b, k]: exact part
-    4 n_i n_j d per selected pair, zeroth-order part 4 n_i |U_i| d, first-order 2 L d^2 per head,
-    statistics 2 x 2 L d^2 per head (K^T V for H-bar and again for M_j), scores 2 N_b^2 d."""
+    4 n_i n_j d per selected pair, zeroth-order part 4 n_i |U_i| d, first-order 2 L d^2 per head
+    (block-wise variant: |U_i| (2 d^2 + 2 d) per query row), statistics 2 x 2 L d^2 per head
+    (K^T V for H-bar and again for M_j), scores 2 N_b^2 d."""
     H, nb, kk = idx.shape
     n = np.full(nb, B, dtype=np.float64)
     n[-1] = L - (nb - 1) * B
@@ -54,7 +55,9 @@ def algorithmic_flops(idx: np.ndarray, L: int, d: int, B: int, phases: int) -> d
     exact = float((4.0 * d * n[None, :] * n_sel).sum())
     tail = kk < nb and (phases & 2)
     zeroth = float(4.0 * d * (n.sum() * (nb - kk)) * H) if tail else 0.0
-    first = float(2.0 * L * d * d * H) if tail and (phases & 4) else 0.0
+    first = 0.0
+    if tail and (phases & 4):
+        first = float(H * L * (nb - kk) * (2.0 * d * d + 2.0 * d)) if first_order else float(2.0 * L * d * d * H)
     stats = float(4.0 * L * d * d * H)
     route = float(2.0 * nb * nb * d * H)
     return {"exact": exact, "zeroth": zeroth, "first": first, "attend": exact + zeroth + first,
@@ -181,10 +184,12 @@ def selection_of(plan, info, H, dev):
     return idx.cpu().numpy()
 
 
-# (label, keep override (None = the workload's), phase mask): the method, its zeroth-order-only
-# ablation, keep-or-drop block-sparse attention at the same k, and dense attention (every block
-# exact) through the same kernel
-MODES = (("pisa", None, 7), ("zeroth-order only", None, 3), ("keep-or-drop", None, 1), ("dense", 1.0, 1))
+# (label, keep override (None = the workload's), phase mask, first order): the method, its
+# block-wise first-order variant (every unselected block's own H_j instead of H-bar), its
+# zeroth-order-only ablation, keep-or-drop block-sparse attention at the same k, and dense
+# attention (every block exact) through the same kernel
+MODES = (("pisa", None, 7, 0), ("block-wise first order", None, 7, 1), ("zeroth-order only", None, 3, 0),
+         ("keep-or-drop", None, 1, 0), ("dense", 1.0, 1, 0))
 
 
 def compare_modes(w, steps, warmup, quality_blocks=8):
@@ -205,14 +210,14 @@ def compare_modes(w, steps, warmup, quality_blocks=8):
                                                                             replace=False))]
     refs = {}
     recs = []
-    for label, keep, phases in MODES:
+    for label, keep, phases, first_order in MODES:
         kp = w.keep if keep is None else keep
-        plan = L.Plan(w.L, w.H, w.d, w.B, kp, dtype=dtype, phases=phases)
+        plan = L.Plan(w.L, w.H, w.d, w.B, kp, dtype=dtype, phases=phases, first_order=first_order)
         plan.attach_workspace(device=dev)
         info = plan.info()
         out = torch.empty_like(qd)
         t = time_stages(plan, qd, kd, vd, out, stream, steps, warmup)
-        fl = algorithmic_flops(selection_of(plan, info, w.H, dev), w.L, w.d, w.B, phases)
+        fl = algorithmic_flops(selection_of(plan, info, w.H, dev), w.L, w.d, w.B, phases, first_order)
         num = den = 0.0
         for h, i in samples:
             rows = np.arange(i * w.B, min(w.L, (i + 1) * w.B))

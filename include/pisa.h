@@ -35,7 +35,8 @@
  * the calling thread's last error text.
  *
  * Supported: dtype bf16 with d = 128, B in {64, 128}; dtype fp32 with d in {64, 128},
- * B in {64, 128}; L >= 1, H >= 1, 0 < keep <= 1, H * L * d < 2^31 elements per tensor.
+ * B in {64, 128}; L >= 1, H >= 1, 0 < keep <= 1, H * L * d < 2^31 elements per tensor;
+ * N_b <= 8192.
  */
 #ifndef PISA_H_
 #define PISA_H_
@@ -63,13 +64,20 @@ typedef enum pisa_option {
   PISA_OPT_DTYPE = 0,   /* PISA_DTYPE_BF16 (default for d = 128) or PISA_DTYPE_F32 (default otherwise) */
   PISA_OPT_SCALE = 1,   /* softmax scale tau > 0 applied to q (default 1/sqrt(d)) */
   PISA_OPT_ROUTING = 2, /* PISA_ROUTING_COV (default) or PISA_ROUTING_PLAIN */
-  PISA_OPT_PHASES = 3   /* bit mask of PISA_PHASE_* (default all three); EXACT must be set */
+  PISA_OPT_PHASES = 3,  /* bit mask of PISA_PHASE_* (default all three); EXACT must be set */
+  PISA_OPT_FIRST_ORDER = 4 /* PISA_FIRST_ORDER_GLOBAL (default) or PISA_FIRST_ORDER_BLOCK */
 } pisa_option;
 
 enum { PISA_DTYPE_BF16 = 0, PISA_DTYPE_F32 = 1 };
 enum { PISA_ROUTING_COV = 0, PISA_ROUTING_PLAIN = 1 };
 /* PHASES = EXACT alone is keep-or-drop block-sparse attention; EXACT|ZEROTH omits H-bar. */
 enum { PISA_PHASE_EXACT = 1, PISA_PHASE_ZEROTH = 2, PISA_PHASE_FIRST = 4 };
+/* First-order term of the unselected blocks. GLOBAL is the method: beta_t (q~_t H-bar), one
+ * shared d x d matrix. BLOCK is the variant the method replaces (gist.science section 2 "Core
+ * algorithm": per-block first-order terms would be memory-bound): sum_{j in U_i} alpha_{t,j}
+ * (q~_t H_j) with every block's own H_j, stored as bf16 in the workspace (N_b d^2 * 2 bytes per
+ * head) and streamed per query block. An ablation; bf16 only. */
+enum { PISA_FIRST_ORDER_GLOBAL = 0, PISA_FIRST_ORDER_BLOCK = 1 };
 
 typedef struct pisa_plan_info {
   int64_t L;
@@ -82,15 +90,17 @@ typedef struct pisa_plan_info {
   size_t workspace_bytes;   /* device bytes pisa_plan_attach_workspace needs (256-B aligned) */
   double flops_stats;       /* 2 * 2 L d^2 per head: K^T V for H-bar and again for M_j */
   double flops_route;       /* 2 N_b^2 d per head */
-  double flops_first;       /* 2 L d^2 per head (q H-bar) */
+  double flops_first;       /* per head: 2 L d^2 (q H-bar); BLOCK: (N_b - k) L (2 d^2 + 2 d) */
   double bytes_stats;       /* compulsory HBM bytes of the statistics kernels (reads Q,K,V,K,V) */
+  int32_t first_order;      /* PISA_FIRST_ORDER_* */
 } pisa_plan_info_t;
 
 /* Create a plan for H heads of L tokens, head dim d, block size B, keeping a fraction `keep` of
  * the N_b key/value blocks per query block. Host only. */
 pisa_status pisa_plan(int64_t L, int32_t H, int32_t d, int32_t B, double keep, pisa_plan_t **plan);
 
-/* Set an option (see pisa_option). Changing the dtype changes workspace_bytes: re-attach. */
+/* Set an option (see pisa_option). Changing the dtype, or selecting the block-wise first-order
+ * variant, changes workspace_bytes: re-attach. */
 pisa_status pisa_plan_set(pisa_plan_t *plan, pisa_option opt, double value);
 
 /* Sizes, derived counts and the FLOP/byte model of the plan. */

@@ -138,7 +138,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
   const size_t head = (size_t)h * dm.L * 128;
   const int32_t* sel = w.idx + ((size_t)h * Nb + i) * kk;
   const bool do_tail = kk < Nb && (dm.phases & 2);
-  const bool do_first = do_tail && (dm.phases & 4);
+  const bool do_first = do_tail && (dm.phases & 4) && !dm.first_block;
+  const bool block_fo = block_first_order(dm);  // per-block first order: finished by first_block_bf16
   const int nc = do_tail ? dm.Nbp / BLK : 0;
   const __bf16* kl = reinterpret_cast<const __bf16*>(w.kbar_lo) + (size_t)h * dm.Nbp * 128;
   const __bf16* vl = reinterpret_cast<const __bf16*>(w.vbar_lo) + (size_t)h * dm.Nbp * 128;
@@ -325,6 +326,26 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
     O[2] += bt * T2[0];
     O[3] += bt * T2[1];
   }
+  if (block_fo) {
+    // hand the unnormalised numerator and (reference, denominator) to the block first-order kernel
+    const uint32_t q = 32 * wave + l32;
+    if ((int)q < n_i) {
+      const size_t row = (size_t)h * dm.L + (size_t)i * B + q;
+      float* orow = w.opart + row * 128;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 v = {O[dt][4 * g], O[dt][4 * g + 1], O[dt][4 * g + 2], O[dt][4 * g + 3]};
+          *reinterpret_cast<f32x4*>(orow + 32 * dt + 8 * g + 4 * hh) = v;
+        }
+      if (hh == 0) {
+        w.ml[2 * row] = m == -INFINITY ? 0.0f : m;
+        w.ml[2 * row + 1] = lsum;
+      }
+    }
+    return;
+  }
   // ---- epilogue: bf16 output rows via LDS (queries 0..63 in one array, 64..127 in the other) --
   const int xs = do_first ? (hstage ^ 1) : 0;
   char* stg_lo = xs ? sK1 : sK0;
@@ -356,7 +377,174 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
   }
 }
 
+// Block-wise first-order variant (an ablation of the global H-bar term): for every unselected
+// block j of the query block, O^T += (alpha_{t,j} scale) (H_j^T Q^T), with alpha_{t,j} relative to
+// the softmax reference the attention kernel used, then out = O / l. One workgroup per (head,
+// query block), BLK/32 waves of 32 queries; H_j^T (bf16, 32 KB) and the centroid row stream
+// through two LDS stages; q . kbar_j is a per-lane dot product over the lane's half of d.
+template <int BLK>
+__global__ __launch_bounds__(BLK * 2, 1) void first_block_bf16(Dims dm, Work w, const __bf16* __restrict__ Q,
+                                                               __bf16* __restrict__ out) {
+  constexpr int NW = BLK / 32;
+  constexpr int NTH = 64 * NW;
+  constexpr int TB = 64 * 256;  // half of H_j^T: 64 rows of 128 bf16
+  __shared__ __attribute__((aligned(1024))) char sA0[TB];
+  __shared__ __attribute__((aligned(1024))) char sB0[TB];
+  __shared__ __attribute__((aligned(1024))) char sA1[TB];
+  __shared__ __attribute__((aligned(1024))) char sB1[TB];
+  __shared__ __attribute__((aligned(1024))) char sk0[1024];  // centroid rows j .. j + 3 (row j used)
+  __shared__ __attribute__((aligned(1024))) char sk1[1024];
+  __shared__ uint32_t selm[kMaskWords];
+  __shared__ uint16_t uidx[8192];
+
+  const int item = blockIdx.x;
+  const int h = item / dm.Nb, i = item % dm.Nb;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t hh = lane >> 5, l32 = lane & 31;
+  const int Nb = dm.Nb, B = dm.B, kk = dm.k;
+  const int n_i = (i == Nb - 1) ? dm.n_last : B;
+  const size_t head = (size_t)h * dm.L * 128;
+  const int32_t* sel = w.idx + ((size_t)h * Nb + i) * kk;
+  const __bf16* hjt = reinterpret_cast<const __bf16*>(w.hjT_lo) + (size_t)h * Nb * 128 * 128;
+  const __bf16* kl = reinterpret_cast<const __bf16*>(w.kbar_lo) + (size_t)h * dm.Nbp * 128;
+
+  // U_i in ascending order: mark S_i, then wave 0 compacts the unmarked blocks with ballots
+  const int nmask = (Nb + 31) / 32;
+  for (int t = tid; t < nmask; t += NTH) selm[t] = 0u;
+  __syncthreads();
+  for (int t = tid; t < kk; t += NTH) {
+    const int j = sel[t];
+    atomicOr(&selm[j >> 5], 1u << (j & 31));
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int base = 0;
+    for (int j0 = 0; j0 < Nb; j0 += 64) {
+      const int j = j0 + lane;
+      const bool in_u = j < Nb && !((selm[j >> 5] >> (j & 31)) & 1u);
+      const uint64_t bal = __ballot(in_u);
+      const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+      if (in_u) uidx[base + before] = (uint16_t)j;
+      base += __popcll(bal);
+    }
+  }
+  __syncthreads();
+  const int nU = Nb - kk;
+
+  const uint32_t vb_row = copy_vbase<false>(wave, lane), vb_row2 = copy_vbase<false>(wave, lane, 8);
+  auto issue = [&](int u, auto stc) {
+    constexpr int ST = decltype(stc)::value;
+    const int j = __builtin_amdgcn_readfirstlane((int)uidx[u]);
+    const __bf16* src = hjt + (size_t)j * 128 * 128;
+    copy_tile<64, NW>(make_rsrc(src, TB), ST ? sA1 : sA0, vb_row, wave, vb_row2);
+    copy_tile<64, NW>(make_rsrc(src + 64 * 128, TB), ST ? sB1 : sB0, vb_row, wave, vb_row2);
+    if (wave == 0) buf_load_lds16(make_rsrc(kl + (size_t)j * 128, (uint32_t)(dm.Nbp - j) * 256), ST ? sk1 : sk0, lane * 16);
+  };
+  issue(0, Stage<0>{});
+
+  bf16x8 qreg[8];
+  const uint32_t q = 32 * wave + l32;
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head + (size_t)i * B * 128, n_i * 256);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, q * 256 + (16 * s + 8 * hh) * 2));
+  }
+  // numerator (exact + zeroth order), reference and denominator from the attention kernel
+  const size_t row0 = (size_t)h * dm.L + (size_t)i * B;
+  f32x16 O[4];
+  {
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(w.opart + row0 * 128, n_i * 512);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x4 v = buf_load16(ro, q * 512 + (32 * dt + 8 * g + 4 * hh) * 4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O[dt][4 * g + r] = __uint_as_float(v[r]);
+      }
+  }
+  float mref = 0.f, lsum = 1.f;
+  if ((int)q < n_i) {
+    mref = w.ml[2 * (row0 + q)];
+    lsum = w.ml[2 * (row0 + q) + 1];
+  }
+  const float cs = dm.scale * kLog2e;
+  const LaneOffsets lofs = lane_offsets(lane);
+
+  auto step = [&](int u, auto stc) {
+    constexpr int ST = decltype(stc)::value;
+    wait_vmem();
+    __syncthreads();  // stage ST landed; the other stage is free
+    if (u + 1 < nU) issue(u + 1, Stage<ST ^ 1>{});
+    // a = q . kbar_j over this lane's half of d, then across the lane pair
+    const char* kr = ST ? sk1 : sk0;
+    float a = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const bf16x8 kv = *reinterpret_cast<const bf16x8*>(kr + (16 * s + 8 * hh) * 2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a = fmaf((float)qreg[s][e], (float)kv[e], a);
+    }
+    a += __shfl_xor(a, 32);
+    const float wgt = __builtin_amdgcn_exp2f(fmaf(a, cs, -mref)) * dm.scale;
+    f32x16 T[2];
+    qk_tile<2>(ST ? sA1 : sA0, 0, qreg, T, lofs);  // (q H_j)[0..63]
+    O[0] += wgt * T[0];
+    O[1] += wgt * T[1];
+    qk_tile<2>(ST ? sB1 : sB0, 0, qreg, T, lofs);  // (q H_j)[64..127]
+    O[2] += wgt * T[0];
+    O[3] += wgt * T[1];
+  };
+  int u = 0;
+  for (; u + 1 < nU; u += 2) {
+    step(u, Stage<0>{});
+    step(u + 1, Stage<1>{});
+  }
+  if (u < nU) step(u, Stage<0>{});
+  __syncthreads();  // every wave done with the stages: reuse them for the output rows
+
+  char* stg_lo = sA0;
+  char* stg_hi = sB0;
+  const float inv_l = 1.0f / lsum;
+  {
+    char* stg = q < 64 ? stg_lo : stg_hi;
+    const uint32_t qr = q & 63;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (__bf16)(O[dt][4 * g + r] * inv_l);
+        const uint32_t byte = (32 * dt + 8 * g + 4 * hh) * 2;
+        *reinterpret_cast<bf16x4*>(stg + qr * 256 + swz_row(qr, byte >> 4) * 16 + (byte & 15)) = v;
+      }
+  }
+  __syncthreads();
+  __bf16* orow = out + head + (size_t)i * B * 128;
+  for (int e = tid; e < n_i * 16; e += NTH) {
+    const uint32_t qq = e >> 4, c = e & 15;
+    const char* stg = qq < 64 ? stg_lo : stg_hi;
+    const uint32_t qr = qq & 63;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + qr * 256 + swz_row(qr, c) * 16);
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(orow) + qq * 256 + c * 16) = v;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_first_block_bf16(const Dims& dm, const Work& w, const void* Q, void* out, hipStream_t s) {
+  const int items = dm.H * dm.Nb;
+  auto q = static_cast<const __bf16*>(Q);
+  auto o = static_cast<__bf16*>(out);
+  if (dm.B == 128)
+    hipLaunchKernelGGL(first_block_bf16<128>, dim3(items), dim3(256), 0, s, dm, w, q, o);
+  else
+    hipLaunchKernelGGL(first_block_bf16<64>, dim3(items), dim3(128), 0, s, dm, w, q, o);
+  return hipGetLastError();
+}
 
 hipError_t launch_attend_bf16(const Dims& dm, const Work& w, const void* Q, const void* K, const void* V, void* out,
                               hipStream_t s) {

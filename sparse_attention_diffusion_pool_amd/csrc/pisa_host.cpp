@@ -2,7 +2,8 @@
 //
 // The plan holds only host state (shapes and options); the caller owns all device memory.
 // pisa_forward enqueues five launches on the caller's stream: block statistics pass, H-bar
-// finalize, block covariance norms, routing, fused piecewise attention.
+// finalize, block covariance norms, routing, fused piecewise attention (plus the per-block
+// first-order kernel when that variant is selected).
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -75,6 +76,13 @@ Layout workspace_layout(const Dims& dm) {
     l.kbar_lo = l.vbar_lo = l.hbarT_lo = (size_t)-1;
   }
   l.idx = take(H * Nb * (size_t)dm.k * 4);
+  if (pisa::block_first_order(dm)) {
+    l.hjT_lo = take(H * Nb * d * d * 2);
+    l.opart = take(H * (size_t)dm.L * d * 4);
+    l.ml = take(H * (size_t)dm.L * 2 * 4);
+  } else {
+    l.hjT_lo = l.opart = l.ml = (size_t)-1;
+  }
   l.total = off;
   return l;
 }
@@ -95,6 +103,11 @@ Work workspace_pointers(const Dims& dm, void* base) {
     w.hbarT_lo = b + l.hbarT_lo;
   }
   w.idx = reinterpret_cast<int32_t*>(b + l.idx);
+  if (block_first_order(dm)) {
+    w.hjT_lo = b + l.hjT_lo;
+    w.opart = reinterpret_cast<float*>(b + l.opart);
+    w.ml = reinterpret_cast<float*>(b + l.ml);
+  }
   return w;
 }
 
@@ -114,6 +127,8 @@ pisa_status check_supported(const pisa::Dims& dm) {
   if (dm.d != 64 && dm.d != 128) return fail(PISA_ERR_UNSUPPORTED, "d must be 64 or 128 (got %d)", dm.d);
   if (dm.B != 64 && dm.B != 128) return fail(PISA_ERR_UNSUPPORTED, "B must be 64 or 128 (got %d)", dm.B);
   if (dm.Nb > 8192) return fail(PISA_ERR_UNSUPPORTED, "at most 8192 blocks per head (got %d)", dm.Nb);
+  if (dm.first_block && dm.dtype != PISA_DTYPE_BF16)
+    return fail(PISA_ERR_UNSUPPORTED, "the block-wise first-order variant is implemented for bf16 only");
   return PISA_OK;
 }
 
@@ -243,6 +258,11 @@ pisa_status pisa_plan_set(pisa_plan_t* p, pisa_option opt, double value) {
       dm.phases = m;
       break;
     }
+    case PISA_OPT_FIRST_ORDER:
+      if (value != PISA_FIRST_ORDER_GLOBAL && value != PISA_FIRST_ORDER_BLOCK)
+        return fail(PISA_ERR_INVALID_ARGUMENT, "first order must be PISA_FIRST_ORDER_GLOBAL or PISA_FIRST_ORDER_BLOCK");
+      dm.first_block = (int)value;
+      break;
     default:
       return fail(PISA_ERR_INVALID_ARGUMENT, "unknown option %d", (int)opt);
   }
@@ -273,8 +293,12 @@ pisa_status pisa_plan_info(const pisa_plan_t* p, pisa_plan_info_t* info) {
   double e = dm.dtype == PISA_DTYPE_BF16 ? 2.0 : 4.0;
   info->flops_stats = H * 2.0 * (2.0 * L * d * d);
   info->flops_route = H * 2.0 * Nb * Nb * d;
-  info->flops_first = (dm.phases & PISA_PHASE_FIRST) ? H * 2.0 * L * d * d : 0.0;
+  const bool tail = dm.k < dm.Nb && (dm.phases & PISA_PHASE_ZEROTH) && (dm.phases & PISA_PHASE_FIRST);
+  info->flops_first = !tail ? 0.0
+                      : dm.first_block ? H * (Nb - dm.k) * L * (2.0 * d * d + 2.0 * d)
+                                       : H * 2.0 * L * d * d;
   info->bytes_stats = H * 5.0 * L * d * e;
+  info->first_order = dm.first_block;
   return PISA_OK;
 }
 
@@ -297,7 +321,7 @@ pisa_status pisa_forward_stats(pisa_plan_t* p, const void* Q, const void* K, con
   pisa::Work w = pisa::workspace_pointers(p->dm, p->ws);
   if ((s = launched(pisa::launch_stats_pass(p->dm, w, Q, K, V, stream), "stats pass")) != PISA_OK) return s;
   if ((s = launched(pisa::launch_stats_finalize(p->dm, w, stream), "H-bar finalize")) != PISA_OK) return s;
-  if (p->dm.routing == PISA_ROUTING_COV)
+  if (p->dm.routing == PISA_ROUTING_COV || pisa::block_first_order(p->dm))
     if ((s = launched(pisa::launch_stats_cov(p->dm, w, K, V, stream), "block covariance norms")) != PISA_OK) return s;
   return PISA_OK;
 }
@@ -318,7 +342,10 @@ pisa_status pisa_forward_attend(pisa_plan_t* p, const void* Q, const void* K, co
   if ((s = check_tensors(p, Q, K, V, out)) != PISA_OK) return s;
   if ((s = check_device()) != PISA_OK) return s;
   pisa::Work w = pisa::workspace_pointers(p->dm, p->ws);
-  return launched(pisa::launch_attend(p->dm, w, Q, K, V, out, stream), "attend");
+  if ((s = launched(pisa::launch_attend(p->dm, w, Q, K, V, out, stream), "attend")) != PISA_OK) return s;
+  if (pisa::block_first_order(p->dm))
+    return launched(pisa::launch_first_block_bf16(p->dm, w, Q, out, stream), "block first order");
+  return PISA_OK;
 }
 
 pisa_status pisa_forward(pisa_plan_t* p, const void* Q, const void* K, const void* V, void* out, hipStream_t stream) {

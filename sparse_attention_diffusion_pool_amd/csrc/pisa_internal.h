@@ -24,7 +24,13 @@ struct Dims {
   int routing; // 0 covariance-aware, 1 plain
   int phases;  // bit mask: 1 exact, 2 zeroth order, 4 first order
   int dtype;   // 0 bf16, 1 fp32
+  int first_block;  // 1: block-wise first-order term (per-block H_j) instead of H-bar
 };
+
+// The block-wise first-order variant runs when it is requested and there is a first-order term.
+__host__ __device__ inline bool block_first_order(const Dims& dm) {
+  return dm.first_block && dm.k < dm.Nb && (dm.phases & 6) == 6;
+}
 
 // Device pointers into the attached workspace.
 struct Work {
@@ -38,10 +44,13 @@ struct Work {
   void* vbar_lo;    // bf16 [H][Nbp][d] value means, zero rows past Nb    (bf16 path only)
   void* hbarT_lo;   // bf16 [H][d][d]   transpose of H-bar                (bf16 path only)
   int32_t* idx;     // [H][Nb][k]   ascending critical block indices
+  void* hjT_lo;     // bf16 [H][Nb][d][d] transposes of every H_j         (block first order only)
+  float* opart;     // [H][L][d]    unnormalised exact + zeroth-order numerator (block first order)
+  float* ml;        // [H][L][2]    softmax reference and denominator        (block first order)
 };
 
 struct Layout {
-  size_t qbar, kbar, vsum, G, hbar, M, kbar_lo, vbar_lo, hbarT_lo, idx, total;
+  size_t qbar, kbar, vsum, G, hbar, M, kbar_lo, vbar_lo, hbarT_lo, idx, hjT_lo, opart, ml, total;
 };
 
 Layout workspace_layout(const Dims& dm);
@@ -56,7 +65,7 @@ hipError_t launch_stats_cov(const Dims& dm, const Work& w, const void* K, const 
                             hipStream_t s);                       // M_j
 hipError_t launch_route(const Dims& dm, const Work& w, hipStream_t s);
 hipError_t launch_attend(const Dims& dm, const Work& w, const void* Q, const void* K,
-                         const void* V, void* out, hipStream_t s);
+                         const void* V, void* out, hipStream_t s);   // + block first order if set
 
 // Per-dtype implementations.
 hipError_t launch_stats_pass_bf16(const Dims&, const Work&, const void*, const void*, const void*, hipStream_t);
@@ -64,6 +73,7 @@ hipError_t launch_stats_cov_bf16(const Dims&, const Work&, const void*, const vo
 hipError_t launch_stats_pass_f32(const Dims&, const Work&, const void*, const void*, const void*, hipStream_t);
 hipError_t launch_stats_cov_f32(const Dims&, const Work&, const void*, const void*, hipStream_t);
 hipError_t launch_attend_bf16(const Dims&, const Work&, const void*, const void*, const void*, void*, hipStream_t);
+hipError_t launch_first_block_bf16(const Dims&, const Work&, const void*, void*, hipStream_t);
 hipError_t launch_attend_f32(const Dims&, const Work&, const void*, const void*, const void*, void*, hipStream_t);
 
 }  // namespace pisa

@@ -9,7 +9,7 @@
 // matrices over its blocks, H_j = K_j^T V_j - kbar_j (sum V_j)^T (= sum_n (k_n - kbar_j)^T v_n).
 // Finalize (per head): H-bar = (sum of the partials) / N_b; bf16 copies of the pooled tokens and
 // of H-bar^T for the attention kernel. Covariance pass (one workgroup per block): H_j again, then
-// M_j = ||H_j - H-bar||_F.
+// M_j = ||H_j - H-bar||_F (and H_j^T in bf16 for the block-wise first-order variant).
 //
 // bf16 inputs: K_j^T V_j on v_mfma_f32_32x32x16_bf16 (products of bf16 values are exact in fp32,
 // accumulation fp32); both operands come from row-major LDS tiles through ds_read_b64_tr_b16.
@@ -191,13 +191,23 @@ __global__ __launch_bounds__(256) void stats_cov_bf16(Dims dm, Work w, const __b
   const float* vs = w.vsum + ((size_t)h * dm.Nb + j) * 128;
   const float* hb = w.hbar + (size_t)h * 128 * 128;
   float ss = 0.f;
+  // block-wise first-order variant: keep H_j^T in bf16 (row b holds H_j[:, b])
+  __bf16* hjt = block_first_order(dm) ? reinterpret_cast<__bf16*>(w.hjT_lo) + ((size_t)h * dm.Nb + j) * 128 * 128
+                                      : nullptr;
   for (int ct = 0; ct < 4; ++ct) {
     const int b = 32 * ct + l32;
     const float vb = vs[b];
-    for (int x = 0; x < 16; ++x) {
-      const int a = 32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3);
-      const float hv = acc[ct][x] - kb[a] * vb - hb[a * 128 + b];
-      ss += hv * hv;
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 hj;
+      for (int r = 0; r < 4; ++r) {
+        const int x = 4 * g + r;
+        const int a = 32 * wave + 8 * g + 4 * hh + r;
+        const float h_ab = acc[ct][x] - kb[a] * vb;
+        const float hv = h_ab - hb[a * 128 + b];
+        ss += hv * hv;
+        hj[r] = (__bf16)h_ab;
+      }
+      if (hjt != nullptr) *reinterpret_cast<bf16x4*>(hjt + b * 128 + 32 * wave + 8 * g + 4 * hh) = hj;
     }
   }
   ss = wave_sum(ss);

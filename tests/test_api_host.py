@@ -62,7 +62,8 @@ def test_plan_info_matches_formulas(Lq, H, d, B, keep):
     assert inf["dtype"] == (0 if d == 128 else 1)
     assert math.isclose(inf["scale"], 1 / math.sqrt(d), rel_tol=1e-7)
     assert inf["workspace_bytes"] % 256 == 0 and inf["workspace_bytes"] > 0
-    assert inf["flops_first"] == H * 2 * Lq * d * d
+    # the first-order term exists only when some block is left unselected
+    assert inf["flops_first"] == (H * 2 * Lq * d * d if inf["k"] < nb else 0)
     assert inf["flops_route"] == H * 2 * nb * nb * d
     p.destroy()
 
@@ -83,6 +84,27 @@ def test_options(lib):
     assert lib_.pisa_plan_set(p.handle, 99, 1.0) == 1
     q = L.Plan(1000, 2, 64, 64, 0.25)
     assert lib_.pisa_plan_set(q.handle, L.OPT_DTYPE, 0.0) == 2  # bf16 needs d = 128
+
+
+def test_block_first_order_option(lib):
+    lib_ = L.load()
+    L_, H, d, B, keep = 1000, 2, 128, 128, 0.25
+    p = L.Plan(L_, H, d, B, keep)
+    w0 = p.info()["workspace_bytes"]
+    assert lib_.pisa_plan_set(p.handle, L.OPT_FIRST_ORDER, 2.0) == 1
+    assert lib_.pisa_plan_set(p.handle, L.OPT_FIRST_ORDER, 1.0) == 0
+    inf = p.info()
+    nb, k = inf["n_blocks"], inf["k"]
+    assert inf["first_order"] == 1
+    assert inf["flops_first"] == H * (nb - k) * L_ * (2 * d * d + 2 * d)
+    # bf16 H_j^T per block, the fp32 numerator and (reference, denominator) per row
+    extra = H * nb * d * d * 2 + H * L_ * d * 4 + H * L_ * 2 * 4
+    assert extra <= inf["workspace_bytes"] - w0 <= extra + 3 * 256
+    assert lib_.pisa_plan_set(p.handle, L.OPT_DTYPE, 1.0) == 2  # the variant is bf16 only
+    assert lib_.pisa_plan_set(p.handle, L.OPT_PHASES, 3.0) == 0  # no first-order term: no extra space
+    assert p.info()["workspace_bytes"] == w0 and p.info()["flops_first"] == 0
+    f = L.Plan(L_, H, 64, B, keep)
+    assert lib_.pisa_plan_set(f.handle, L.OPT_FIRST_ORDER, 1.0) == 2
 
 
 def test_workspace_and_pointer_checks(lib):

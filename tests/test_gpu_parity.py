@@ -85,6 +85,37 @@ def test_small_bf16_modes(phases, routing):
 
 
 # ---------------------------------------------------------------------------------------------
+# Block-wise first-order variant (per-block H_j instead of H-bar), against the oracle's
+# first_order="block" mode; with the first-order phase off the option changes nothing.
+# ---------------------------------------------------------------------------------------------
+
+BLOCK_FO = [c for c in SMALL if c[0] in ("bf16-ragged-3d", "bf16-B64-text", "bf16-k1", "bf16-two-pooled-tiles")]
+
+
+@pytest.mark.parametrize("case", BLOCK_FO, ids=[c[0] for c in BLOCK_FO])
+def test_small_block_first_order(case):
+    name, H, grid, n_text, d, B, keep, dtype = case
+    w = custom(name, H, grid, d, B, keep, dtype, n_text=n_text)
+    res = gpu_run(w, want_stats=True, first_order=1)
+    _full_check(res, label=f"{name} block first order")
+
+
+def test_block_first_order_inactive_without_first_phase():
+    w = custom("bf16-modes", 2, (7, 11, 13), 128, 128, 0.3, "bf16")
+    inputs = layer_inputs(w)
+    a = gpu_run(w, inputs=inputs, phases=3)
+    b = gpu_run(w, inputs=inputs, phases=3, first_order=1)
+    assert torch.equal(a["out"], b["out"])
+
+
+def test_block_first_order_wan720p():
+    w = CONFIGS[3]
+    res = gpu_run(w, heads=[0, 17], first_order=1)
+    qb = sample_blocks(res["info"]["n_blocks"], 6, seed=31)
+    _full_check(res, label=f"{w.name} block first order", query_blocks=qb, stats=False)
+
+
+# ---------------------------------------------------------------------------------------------
 # FLUX-like layer (24 heads, L = 4608, B = 64): every head's selection, four heads' outputs.
 # ---------------------------------------------------------------------------------------------
 
