@@ -246,6 +246,61 @@ def compare_modes(w, steps, warmup, quality_blocks=8):
     return recs
 
 
+ROUTINGS = (("covariance-aware, Frobenius M_j", 0, 0), ("covariance-aware, spectral M_j", 0, 1),
+            ("plain (pooled q . k only)", 1, 0))
+
+
+def routing_quality(w, sharpen, steps, warmup, quality_blocks=8):
+    """Routing variants on one workload: relative L2 error against fp64 dense attention (the method
+    and keep-or-drop with each routing's own selection) and the statistics + routing time. Q is
+    multiplied by `sharpen` (scores scale with it: larger values give peakier attention)."""
+    import torch
+    from sparse_attention_diffusion_pool_amd import _lib as L
+    from workloads import layer_inputs
+    q, k, v = layer_inputs(w)
+    if sharpen != 1.0:
+        q = (q.float() * sharpen).to(q.dtype)
+    dev = torch.device("cuda", 0)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    stream = torch.cuda.current_stream()
+    dtype = L.DTYPE_BF16 if w.dtype == "bf16" else L.DTYPE_F32
+    rng = np.random.default_rng(0)
+    nb = -(-w.L // w.B)
+    samples = [(h, int(i)) for h in (0, w.H - 1) for i in sorted(rng.choice(nb, size=min(quality_blocks, nb),
+                                                                            replace=False))]
+    scale = 1.0 / math.sqrt(w.d)
+    refs = {(h, i): dense_rows(q[h], k[h], v[h], np.arange(i * w.B, min(w.L, (i + 1) * w.B)), scale)
+            for h, i in samples}
+    den = sum(float((r ** 2).sum()) for r in refs.values())
+    print(f"workload {w.name} (H={w.H}, L={w.L}, keep={w.keep}), Q scaled by {sharpen:g}; relative L2 "
+          f"against fp64 dense attention on {len(samples)} query blocks of heads 0 and {w.H - 1}; "
+          f"statistics + routing ms: mean of {steps} calls after {warmup} warm-up\n")
+    print("| routing | method rel-L2 | keep-or-drop rel-L2 | statistics + routing ms |")
+    print("|---|---|---|---|")
+    recs = []
+    for label, routing, norm in ROUTINGS:
+        errs = {}
+        t_sr = None
+        for phases in (7, 1):
+            plan = L.Plan(w.L, w.H, w.d, w.B, w.keep, dtype=dtype, phases=phases, routing=routing, norm=norm)
+            plan.attach_workspace(device=dev)
+            out = torch.empty_like(qd)
+            t = time_stages(plan, qd, kd, vd, out, stream, steps, warmup)
+            if phases == 7:
+                t_sr = float((t["stats"] + t["route"]).mean())
+            num = 0.0
+            for (h, i), ref in refs.items():
+                rows = np.arange(i * w.B, min(w.L, (i + 1) * w.B))
+                got = out[h, rows[0]:rows[-1] + 1].to(torch.float64).cpu()
+                num += float(((got - ref) ** 2).sum())
+            errs[phases] = math.sqrt(num / den)
+            plan.destroy()
+            del out
+        recs.append((label, errs[7], errs[1], t_sr))
+        print(f"| {label} | {errs[7]:.4f} | {errs[1]:.4f} | {t_sr:.3f} |")
+    return recs
+
+
 SWEEP_GRIDS = ((4, 32, 32), (8, 32, 32), (16, 32, 32), (32, 32, 32))   # L = 4K, 8K, 16K, 32K
 SWEEP_KEEP = (0.05, 0.1, 0.125, 0.2, 0.3, 0.5)
 
@@ -299,6 +354,9 @@ def main():
     ap.add_argument("--no-quality", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=5)
     ap.add_argument("--phases", type=int, default=7)
+    ap.add_argument("--routing", choices=("cov", "plain"), default="cov")
+    ap.add_argument("--norm", choices=("fro", "spectral"), default="fro", help="matrix norm in M_j")
+    ap.add_argument("--first-order", choices=("global", "block"), default="global")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (scales the HBM byte counters)")
     ap.add_argument("--summarize-trace", metavar="DIR",
@@ -313,6 +371,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="latency over L = 4K..32K and keep 0.05..0.5 against dense (markdown table) and exit")
     ap.add_argument("--sweep-heads", type=int, default=24)
+    ap.add_argument("--routing-quality", action="store_true",
+                    help="compare routing variants (error vs dense, statistics + routing time) and exit")
+    ap.add_argument("--sharpen", type=float, default=1.0, help="multiply Q by this factor (--routing-quality)")
     args = ap.parse_args()
 
     if args.summarize_trace:
@@ -345,6 +406,10 @@ def main():
     if args.sweep:
         latency_sweep(args.sweep_heads, args.steps, args.warmup)
         return
+    if args.routing_quality:
+        from workloads import CONFIGS
+        routing_quality(CONFIGS[args.workload], args.sharpen, args.steps, args.warmup)
+        return
 
     import torch
     from sparse_attention_diffusion_pool_amd import _lib as L
@@ -357,7 +422,10 @@ def main():
     dev = torch.device("cuda", 0)
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     dtype = L.DTYPE_BF16 if w.dtype == "bf16" else L.DTYPE_F32
-    plan = L.Plan(w.L, w.H, w.d, w.B, w.keep, dtype=dtype, phases=args.phases)
+    first_order = 1 if args.first_order == "block" else 0
+    plan = L.Plan(w.L, w.H, w.d, w.B, w.keep, dtype=dtype, phases=args.phases,
+                  routing=1 if args.routing == "plain" else 0, norm=1 if args.norm == "spectral" else 0,
+                  first_order=first_order)
     plan.attach_workspace(device=dev)
     info = plan.info()
     out = torch.empty_like(qd)
@@ -369,14 +437,15 @@ def main():
     step_ms, stats_ms, route_ms, attend_ms = t["step"], t["stats"], t["route"], t["attend"]
     ms_per_step = t["span"] / K
 
-    fl = algorithmic_flops(selection_of(plan, info, w.H, dev), w.L, w.d, w.B, args.phases)
+    fl = algorithmic_flops(selection_of(plan, info, w.H, dev), w.L, w.d, w.B, args.phases, first_order)
     tflops = fl["total"] / (ms_per_step * 1e-3) / 1e12
     attend_tflops = fl["attend"] / (attend_ms.mean() * 1e-3) / 1e12
     stats_gbps = info["bytes_stats"] / (stats_ms.mean() * 1e-3) / 1e9
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_VALU_TFLOPS
 
     traffic = None
-    if os.path.exists(TRAFFIC_FILE) and w.cfg_id == 3:
+    default_mode = args.phases == 7 and args.routing == "cov" and args.norm == "fro" and first_order == 0
+    if os.path.exists(TRAFFIC_FILE) and w.cfg_id == 3 and default_mode:
         tr = json.load(open(TRAFFIC_FILE))
         if tr.get("source_sha") == source_sha(ATTEND_SRC):
             traffic = tr.get("hbm_bytes_per_launch")
@@ -395,7 +464,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded random-Fourier-feature Q/K of the layer's token grid, V ~ N(0,1))",
         "config": {"workload": w.name, "H": w.H, "L": w.L, "d": w.d, "B": w.B, "keep": w.keep,
-                   "n_blocks": info["n_blocks"], "k": info["k"], "phases": args.phases},
+                   "n_blocks": info["n_blocks"], "k": info["k"], "phases": args.phases,
+                   "routing": args.routing, "norm": args.norm, "first_order": args.first_order},
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "ms": {"step_median": round(float(np.median(step_ms)), 4), "step_min": round(float(step_ms.min()), 4),
                "stats": round(float(stats_ms.mean()), 4), "route": round(float(route_ms.mean()), 4),

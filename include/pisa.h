@@ -8,8 +8,8 @@
  *     key/value blocks, computed exactly; the other blocks U_i are approximated.
  *   - Precompute (gist.science section 2 "Hardware implementation"): per block the key centroid
  *     kbar_j, the value sum, the block first-order matrix H_j = sum_n (k_n - kbar_j)^T v_n, their
- *     mean H-bar over all blocks, and M_j = ||H_j - H-bar||_F for routing (section 2
- *     "Covariance-aware routing").
+ *     mean H-bar over all blocks, and M_j = ||H_j - H-bar|| for routing (section 2
+ *     "Covariance-aware routing"; Frobenius norm by default, spectral as an option).
  *   - Routing: S_i = the k largest Score_{i,j} = qbar_i . kbar_j + ln(n_j + ||qbar_i|| M_j)
  *     (qbar_i = mean scaled query of block i; ties to the lower j). The pages name the score's
  *     ingredients but print no formula: this is the library's reading (PISA_ROUTING_PLAIN drops
@@ -65,7 +65,8 @@ typedef enum pisa_option {
   PISA_OPT_SCALE = 1,   /* softmax scale tau > 0 applied to q (default 1/sqrt(d)) */
   PISA_OPT_ROUTING = 2, /* PISA_ROUTING_COV (default) or PISA_ROUTING_PLAIN */
   PISA_OPT_PHASES = 3,  /* bit mask of PISA_PHASE_* (default all three); EXACT must be set */
-  PISA_OPT_FIRST_ORDER = 4 /* PISA_FIRST_ORDER_GLOBAL (default) or PISA_FIRST_ORDER_BLOCK */
+  PISA_OPT_FIRST_ORDER = 4, /* PISA_FIRST_ORDER_GLOBAL (default) or PISA_FIRST_ORDER_BLOCK */
+  PISA_OPT_NORM = 5         /* matrix norm in M_j: PISA_NORM_FROBENIUS (default) or PISA_NORM_SPECTRAL */
 } pisa_option;
 
 enum { PISA_DTYPE_BF16 = 0, PISA_DTYPE_F32 = 1 };
@@ -78,6 +79,12 @@ enum { PISA_PHASE_EXACT = 1, PISA_PHASE_ZEROTH = 2, PISA_PHASE_FIRST = 4 };
  * (q~_t H_j) with every block's own H_j, stored as bf16 in the workspace (N_b d^2 * 2 bytes per
  * head) and streamed per query block. An ablation; bf16 only. */
 enum { PISA_FIRST_ORDER_GLOBAL = 0, PISA_FIRST_ORDER_BLOCK = 1 };
+/* The covariance-aware routing section of the gist.science summary writes M_j with a 2-norm
+ * of a matrix. FROBENIUS reads it as ||.||_F (cheap, and an upper bound of the spectral norm);
+ * SPECTRAL computes the largest singular value of H_j - H-bar (Lanczos on its Gram matrix, at
+ * most 32 steps with full reorthogonalisation, then bisection on the tridiagonal: about 1e-6
+ * relative for well-separated top singular values). Used by PISA_ROUTING_COV only. */
+enum { PISA_NORM_FROBENIUS = 0, PISA_NORM_SPECTRAL = 1 };
 
 typedef struct pisa_plan_info {
   int64_t L;
@@ -93,6 +100,7 @@ typedef struct pisa_plan_info {
   double flops_first;       /* per head: 2 L d^2 (q H-bar); BLOCK: (N_b - k) L (2 d^2 + 2 d) */
   double bytes_stats;       /* compulsory HBM bytes of the statistics kernels (reads Q,K,V,K,V) */
   int32_t first_order;      /* PISA_FIRST_ORDER_* */
+  int32_t norm;             /* PISA_NORM_* */
 } pisa_plan_info_t;
 
 /* Create a plan for H heads of L tokens, head dim d, block size B, keeping a fraction `keep` of

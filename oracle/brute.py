@@ -9,6 +9,7 @@ Written independently of ``pisa_oracle`` (no NumPy, no shared helpers) to pin it
   ``first_order="block"`` this is the expansion itself, with ``"global"`` the per-block
   first-order numerator part is replaced by the H-bar term, with ``"none"`` dropped).
 * ``route``: scores and the (score desc, index asc) top-k by a full sort.
+* ``spectral_norm``: largest singular value by power iteration (the spectral reading of M_j).
 
 Inputs are lists of lists of floats (or anything indexable that yields floats).
 """
@@ -50,6 +51,24 @@ def block_stats(q, k, v, B, scale):
          for j in range(nb)]
     return {"n": n, "kbar": kbar, "vsum": vsum, "qbar": qbar, "H": H, "Hbar": Hbar, "M": M,
             "blocks": bl}
+
+
+def spectral_norm(E, iters=4000):
+    """Largest singular value of a small square matrix (list of rows) by plain power iteration on
+    E^T E from the all-ones vector, then sqrt of the Rayleigh quotient."""
+    d = len(E)
+    x = [1.0] * d
+    lam = 0.0
+    for _ in range(iters):
+        y = [sum(E[r][c] * x[c] for c in range(d)) for r in range(d)]      # E x
+        z = [sum(E[r][c] * y[r] for r in range(d)) for c in range(d)]      # E^T E x
+        nz = math.sqrt(sum(t * t for t in z))
+        if nz == 0.0:
+            return 0.0
+        nx = math.sqrt(sum(t * t for t in x))
+        lam = sum(a * b for a, b in zip(x, z)) / (nx * nx)
+        x = [t / nz for t in z]
+    return math.sqrt(max(lam, 0.0))
 
 
 def route(st, k_top, routing="cov"):

@@ -19,7 +19,8 @@ DTYPE_BF16, DTYPE_F32 = 0, 1
 ROUTING_COV, ROUTING_PLAIN = 0, 1
 PHASE_EXACT, PHASE_ZEROTH, PHASE_FIRST = 1, 2, 4
 FIRST_ORDER_GLOBAL, FIRST_ORDER_BLOCK = 0, 1
-OPT_DTYPE, OPT_SCALE, OPT_ROUTING, OPT_PHASES, OPT_FIRST_ORDER = 0, 1, 2, 3, 4
+NORM_FROBENIUS, NORM_SPECTRAL = 0, 1
+OPT_DTYPE, OPT_SCALE, OPT_ROUTING, OPT_PHASES, OPT_FIRST_ORDER, OPT_NORM = 0, 1, 2, 3, 4, 5
 
 
 class PisaError(RuntimeError):
@@ -35,7 +36,7 @@ class PlanInfo(ctypes.Structure):
                 ("phases", ctypes.c_int32), ("scale", ctypes.c_double),
                 ("workspace_bytes", ctypes.c_size_t), ("flops_stats", ctypes.c_double),
                 ("flops_route", ctypes.c_double), ("flops_first", ctypes.c_double),
-                ("bytes_stats", ctypes.c_double), ("first_order", ctypes.c_int32)]
+                ("bytes_stats", ctypes.c_double), ("first_order", ctypes.c_int32), ("norm", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -121,14 +122,14 @@ class Plan:
     """A libpisa plan. Tensors are passed as torch tensors (device memory) or raw addresses."""
 
     def __init__(self, L: int, H: int, d: int, B: int, keep: float, dtype=None, scale=None,
-                 routing=None, phases=None, first_order=None):
+                 routing=None, phases=None, first_order=None, norm=None):
         lib = load()
         h = _P()
         check(lib.pisa_plan(int(L), int(H), int(d), int(B), float(keep), ctypes.byref(h)), "pisa_plan")
         self._h = h
         self._ws = None
         for opt, val in ((OPT_DTYPE, dtype), (OPT_SCALE, scale), (OPT_ROUTING, routing),
-                         (OPT_PHASES, phases), (OPT_FIRST_ORDER, first_order)):
+                         (OPT_PHASES, phases), (OPT_FIRST_ORDER, first_order), (OPT_NORM, norm)):
             if val is not None:
                 check(lib.pisa_plan_set(self._h, opt, float(val)), "pisa_plan_set")
 

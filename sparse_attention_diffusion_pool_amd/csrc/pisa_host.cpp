@@ -258,6 +258,11 @@ pisa_status pisa_plan_set(pisa_plan_t* p, pisa_option opt, double value) {
       dm.phases = m;
       break;
     }
+    case PISA_OPT_NORM:
+      if (value != PISA_NORM_FROBENIUS && value != PISA_NORM_SPECTRAL)
+        return fail(PISA_ERR_INVALID_ARGUMENT, "norm must be PISA_NORM_FROBENIUS or PISA_NORM_SPECTRAL");
+      dm.spectral = (int)value;
+      break;
     case PISA_OPT_FIRST_ORDER:
       if (value != PISA_FIRST_ORDER_GLOBAL && value != PISA_FIRST_ORDER_BLOCK)
         return fail(PISA_ERR_INVALID_ARGUMENT, "first order must be PISA_FIRST_ORDER_GLOBAL or PISA_FIRST_ORDER_BLOCK");
@@ -299,6 +304,7 @@ pisa_status pisa_plan_info(const pisa_plan_t* p, pisa_plan_info_t* info) {
                                        : H * 2.0 * L * d * d;
   info->bytes_stats = H * 5.0 * L * d * e;
   info->first_order = dm.first_block;
+  info->norm = dm.spectral;
   return PISA_OK;
 }
 

@@ -25,6 +25,7 @@ struct Dims {
   int phases;  // bit mask: 1 exact, 2 zeroth order, 4 first order
   int dtype;   // 0 bf16, 1 fp32
   int first_block;  // 1: block-wise first-order term (per-block H_j) instead of H-bar
+  int spectral;     // 1: M_j = spectral norm of H_j - H-bar (default Frobenius)
 };
 
 // The block-wise first-order variant runs when it is requested and there is a first-order term.

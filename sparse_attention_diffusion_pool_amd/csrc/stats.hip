@@ -169,12 +169,170 @@ __global__ __launch_bounds__(256) void stats_pass_bf16(Dims dm, Work w, const __
     }
 }
 
-template <int BLK>
+// ---------------------------------------------------------------------------------------------
+// Spectral-norm variant of M_j: the largest singular value of E = H_j - H-bar. Lanczos on E^T E
+// (Krylov basis from a fixed start vector, both Gram-Schmidt passes repeated against every basis
+// vector), at most kLanczos steps or until the basis spans an invariant subspace, then the largest
+// eigenvalue of the Lanczos tridiagonal by 64-lane multisection on its Sturm count. E (row stride
+// D + 1 floats), the basis and the scratch live in LDS; all 256 threads call it.
+// ---------------------------------------------------------------------------------------------
+
+constexpr int kLanczos = 32;
+
+template <int D>
+struct SpecLds {
+  float E[D][D + 1];
+  float Qb[kLanczos + 1][D + 1];  // Lanczos basis, one vector per row
+  float u[D], w[D];
+  float part[256 / D][D];
+  float coef[kLanczos + 1];
+  float alpha[kLanczos], beta[kLanczos];
+  float red[4];
+  float lo_hi[2];
+  int m;
+};
+
+// number of eigenvalues below x of the symmetric tridiagonal (a[0..m-1], off-diagonal b[0..m-2])
+__device__ __forceinline__ int sturm_count(const float* a, const float* b, int m, float x) {
+  float d = a[0] - x;
+  int cnt = d < 0.f;
+  for (int i = 1; i < m; ++i) {
+    if (d == 0.f) d = 1e-30f;
+    d = a[i] - x - b[i - 1] * b[i - 1] / d;
+    cnt += d < 0.f;
+  }
+  return cnt;
+}
+
+template <int D>
+__device__ float spectral_norm(SpecLds<D>& S, int tid) {
+  constexpr int TPR = 256 / D;   // threads per row / column
+  constexpr int SEG = D / TPR;
+  const int lane = tid & 63, wave = tid >> 6;
+  auto block_sum = [&](float x) {  // sum over all 256 threads
+    x = wave_sum(x);
+    __syncthreads();
+    if (lane == 0) S.red[wave] = x;
+    __syncthreads();
+    return S.red[0] + S.red[1] + S.red[2] + S.red[3];
+  };
+  // ||E||_F^2 sets the scale of the breakdown test; fixed start vector 1 + cos(r), normalised
+  float fro = 0.f;
+  for (int e = tid; e < D * D; e += 256) fro += S.E[e / D][e % D] * S.E[e / D][e % D];
+  fro = block_sum(fro);
+  if (!(fro > 0.f)) return 0.f;
+  float q0 = 0.f;
+  if (tid < D) q0 = 1.0f + __cosf((float)tid);
+  const float n0 = block_sum(q0 * q0);
+  if (tid < D) S.Qb[0][tid] = q0 * rsqrtf(n0);
+  __syncthreads();
+  const int K = D < kLanczos ? D : kLanczos;
+  int m = K;
+  for (int k = 0; k < K; ++k) {
+    {  // u = E q_k (four independent partial sums keep several LDS reads in flight)
+      const int r = tid / TPR, pt = tid % TPR;
+      float a4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int c = pt * SEG; c < (pt + 1) * SEG; c += 4)
+        for (int x = 0; x < 4; ++x) a4[x] = fmaf(S.E[r][c + x], S.Qb[k][c + x], a4[x]);
+      float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+      for (int o = 1; o < TPR; o <<= 1) acc += __shfl_xor(acc, o);
+      if (pt == 0) S.u[r] = acc;
+    }
+    __syncthreads();
+    {  // w = E^T u (partials over row segments)
+      const int c = tid % D, pt = tid / D;
+      float a4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int r = pt * SEG; r < (pt + 1) * SEG; r += 4)
+        for (int x = 0; x < 4; ++x) a4[x] = fmaf(S.E[r + x][c], S.u[r + x], a4[x]);
+      S.part[pt][c] = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+    }
+    __syncthreads();
+    if (tid < D) {
+      float acc = 0.f;
+      for (int pt = 0; pt < TPR; ++pt) acc += S.part[pt][tid];
+      S.w[tid] = acc;
+    }
+    __syncthreads();
+    float a_k = 0.f;
+    for (int pass = 0; pass < 2; ++pass) {  // w -= Q (Q^T w), twice
+      {
+        const int i = tid / TPR, pt = tid % TPR;
+        float a4[4] = {0.f, 0.f, 0.f, 0.f};
+        if (i <= k) {
+#pragma unroll 4
+          for (int r = pt * SEG; r < (pt + 1) * SEG; r += 4)
+            for (int x = 0; x < 4; ++x) a4[x] = fmaf(S.Qb[i][r + x], S.w[r + x], a4[x]);
+        }
+        float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
+        for (int o = 1; o < TPR; o <<= 1) acc += __shfl_xor(acc, o);
+        if (pt == 0 && i <= k) S.coef[i] = acc;
+      }
+      __syncthreads();
+      a_k += S.coef[k];
+      {
+        const int r = tid % D, pt = tid / D;
+        float a2[2] = {0.f, 0.f};
+        int i = pt;
+        for (; i + TPR <= k; i += 2 * TPR) {
+          a2[0] = fmaf(S.coef[i], S.Qb[i][r], a2[0]);
+          a2[1] = fmaf(S.coef[i + TPR], S.Qb[i + TPR][r], a2[1]);
+        }
+        if (i <= k) a2[0] = fmaf(S.coef[i], S.Qb[i][r], a2[0]);
+        S.part[pt][r] = a2[0] + a2[1];
+      }
+      __syncthreads();
+      if (tid < D) {
+        float acc = 0.f;
+        for (int pt = 0; pt < TPR; ++pt) acc += S.part[pt][tid];
+        S.w[tid] -= acc;
+      }
+      __syncthreads();
+    }
+    const float wr = tid < D ? S.w[tid] : 0.f;
+    const float b_k = sqrtf(block_sum(wr * wr));
+    if (tid == 0) {
+      S.alpha[k] = a_k;
+      S.beta[k] = b_k;
+    }
+    if (b_k <= 1e-6f * fro || k == K - 1) {  // invariant subspace reached (or last step)
+      m = k + 1;
+      break;
+    }
+    if (tid < D) S.Qb[k + 1][tid] = wr / b_k;
+    __syncthreads();
+  }
+  __syncthreads();
+  // largest eigenvalue of the tridiagonal: eigenvalues of E^T E lie in [0, ||E||_F^2]
+  if (wave == 0) {
+    float lo = 0.f, hi = fro * 1.0001f;
+    for (int it = 0; it < 6; ++it) {
+      const float x = lo + (hi - lo) * (float)(lane + 1) / 65.0f;
+      const bool all_below = sturm_count(S.alpha, S.beta, m, x) == m;
+      const uint64_t bal = __ballot(all_below);
+      const int first = bal ? __builtin_ctzll(bal) : 64;
+      const float nhi = first < 64 ? lo + (hi - lo) * (float)(first + 1) / 65.0f : hi;
+      const float nlo = first > 0 ? lo + (hi - lo) * (float)first / 65.0f : lo;
+      lo = nlo;
+      hi = nhi;
+    }
+    if (lane == 0) {
+      S.lo_hi[0] = lo;
+      S.lo_hi[1] = hi;
+    }
+  }
+  __syncthreads();
+  return sqrtf(0.5f * (S.lo_hi[0] + S.lo_hi[1]));
+}
+
+template <int BLK, bool SPEC>
 __global__ __launch_bounds__(256) void stats_cov_bf16(Dims dm, Work w, const __bf16* __restrict__ K,
                                                       const __bf16* __restrict__ V) {
   __shared__ __attribute__((aligned(1024))) char Ks[BLK * 256];
   __shared__ __attribute__((aligned(1024))) char Vs[BLK * 256];
   __shared__ float red[4];
+  __shared__ SpecLds<SPEC ? 128 : 1> spec;
   const int h = blockIdx.y, j = blockIdx.x;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = (j == dm.Nb - 1) ? dm.n_last : dm.B;
@@ -206,9 +364,16 @@ __global__ __launch_bounds__(256) void stats_cov_bf16(Dims dm, Work w, const __b
         const float hv = h_ab - hb[a * 128 + b];
         ss += hv * hv;
         hj[r] = (__bf16)h_ab;
+        if constexpr (SPEC) spec.E[a][b] = hv;
       }
       if (hjt != nullptr) *reinterpret_cast<bf16x4*>(hjt + b * 128 + 32 * wave + 8 * g + 4 * hh) = hj;
     }
+  }
+  if constexpr (SPEC) {
+    __syncthreads();
+    const float sn = spectral_norm<128>(spec, tid);
+    if (tid == 0) w.M[(size_t)h * dm.Nb + j] = sn;
+    return;
   }
   ss = wave_sum(ss);
   if (lane == 0) red[wave] = ss;
@@ -220,7 +385,7 @@ __global__ __launch_bounds__(256) void stats_cov_bf16(Dims dm, Work w, const __b
 // fp32 inputs: plain FMA. Each thread owns a P x P patch of the D x D product (P = D / 16).
 // ---------------------------------------------------------------------------------------------
 
-template <int D, bool COV>
+template <int D, bool COV, bool SPEC = false>
 __global__ __launch_bounds__(256) void stats_f32(Dims dm, Work w, const float* __restrict__ Q,
                                                  const float* __restrict__ K, const float* __restrict__ V) {
   constexpr int P = D / 16;
@@ -228,6 +393,7 @@ __global__ __launch_bounds__(256) void stats_f32(Dims dm, Work w, const float* _
   __shared__ float Ks[SUB][D + 4];
   __shared__ float Vs[SUB][D + 4];
   __shared__ float red[256 / 64];
+  __shared__ SpecLds<SPEC ? D : 1> spec;
   __shared__ float ckb[D], cvs[D];  // centroid and value sum of the current block (pass A)
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
@@ -292,7 +458,14 @@ __global__ __launch_bounds__(256) void stats_f32(Dims dm, Work w, const float* _
         for (int y = 0; y < P; ++y) {
           const float hv = acc[x][y] - kb[a0 + x] * vs[b0 + y] - hb[(a0 + x) * D + b0 + y];
           ss += hv * hv;
+          if constexpr (SPEC) spec.E[a0 + x][b0 + y] = hv;
         }
+      if constexpr (SPEC) {
+        __syncthreads();
+        const float sn = spectral_norm<D>(spec, tid);
+        if (tid == 0) w.M[(size_t)h * dm.Nb + j] = sn;
+        continue;
+      }
       ss = wave_sum(ss);
       if ((tid & 63) == 0) red[tid >> 6] = ss;
       __syncthreads();
@@ -369,10 +542,17 @@ hipError_t launch_stats_cov_bf16(const Dims& dm, const Work& w, const void* K, c
   dim3 grid(dm.Nb, dm.H);
   auto k = static_cast<const __bf16*>(K);
   auto v = static_cast<const __bf16*>(V);
-  if (dm.B == 128)
-    hipLaunchKernelGGL(stats_cov_bf16<128>, grid, dim3(256), 0, s, dm, w, k, v);
-  else
-    hipLaunchKernelGGL(stats_cov_bf16<64>, grid, dim3(256), 0, s, dm, w, k, v);
+  if (dm.spectral) {
+    if (dm.B == 128)
+      hipLaunchKernelGGL((stats_cov_bf16<128, true>), grid, dim3(256), 0, s, dm, w, k, v);
+    else
+      hipLaunchKernelGGL((stats_cov_bf16<64, true>), grid, dim3(256), 0, s, dm, w, k, v);
+  } else {
+    if (dm.B == 128)
+      hipLaunchKernelGGL((stats_cov_bf16<128, false>), grid, dim3(256), 0, s, dm, w, k, v);
+    else
+      hipLaunchKernelGGL((stats_cov_bf16<64, false>), grid, dim3(256), 0, s, dm, w, k, v);
+  }
   return hipGetLastError();
 }
 
@@ -393,10 +573,17 @@ hipError_t launch_stats_cov_f32(const Dims& dm, const Work& w, const void* K, co
   dim3 grid(dm.Nb, dm.H);
   auto k = static_cast<const float*>(K);
   auto v = static_cast<const float*>(V);
-  if (dm.d == 128)
-    hipLaunchKernelGGL((stats_f32<128, true>), grid, dim3(256), 0, s, dm, w, nullptr, k, v);
-  else
-    hipLaunchKernelGGL((stats_f32<64, true>), grid, dim3(256), 0, s, dm, w, nullptr, k, v);
+  if (dm.spectral) {
+    if (dm.d == 128)
+      hipLaunchKernelGGL((stats_f32<128, true, true>), grid, dim3(256), 0, s, dm, w, nullptr, k, v);
+    else
+      hipLaunchKernelGGL((stats_f32<64, true, true>), grid, dim3(256), 0, s, dm, w, nullptr, k, v);
+  } else {
+    if (dm.d == 128)
+      hipLaunchKernelGGL((stats_f32<128, true>), grid, dim3(256), 0, s, dm, w, nullptr, k, v);
+    else
+      hipLaunchKernelGGL((stats_f32<64, true>), grid, dim3(256), 0, s, dm, w, nullptr, k, v);
+  }
   return hipGetLastError();
 }
 

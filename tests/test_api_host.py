@@ -86,6 +86,16 @@ def test_options(lib):
     assert lib_.pisa_plan_set(q.handle, L.OPT_DTYPE, 0.0) == 2  # bf16 needs d = 128
 
 
+def test_norm_option(lib):
+    lib_ = L.load()
+    p = L.Plan(1000, 2, 128, 128, 0.25)
+    w0 = p.info()["workspace_bytes"]
+    assert p.info()["norm"] == 0
+    assert lib_.pisa_plan_set(p.handle, L.OPT_NORM, 2.0) == 1
+    assert lib_.pisa_plan_set(p.handle, L.OPT_NORM, 1.0) == 0
+    assert p.info()["norm"] == 1 and p.info()["workspace_bytes"] == w0
+
+
 def test_block_first_order_option(lib):
     lib_ = L.load()
     L_, H, d, B, keep = 1000, 2, 128, 128, 0.25

@@ -116,6 +116,32 @@ def test_block_first_order_wan720p():
 
 
 # ---------------------------------------------------------------------------------------------
+# Spectral-norm M_j (covariance routing with the largest singular value of H_j - H-bar).
+# ---------------------------------------------------------------------------------------------
+
+def test_tiny_fp32_spectral():
+    w = CONFIGS[0]
+    res = gpu_run(w, want_stats=True, norm=1)
+    _full_check(res, label=f"{w.name} spectral")
+
+
+@pytest.mark.parametrize("case", [c for c in SMALL if c[0] in ("bf16-ragged-3d", "bf16-B64-text", "f32-d64-B128")],
+                         ids=["bf16-ragged-3d", "bf16-B64-text", "f32-d64-B128"])
+def test_small_spectral(case):
+    name, H, grid, n_text, d, B, keep, dtype = case
+    w = custom(name, H, grid, d, B, keep, dtype, n_text=n_text)
+    res = gpu_run(w, want_stats=True, norm=1)
+    _full_check(res, label=f"{name} spectral")
+
+
+def test_spectral_wan720p_selection():
+    w = CONFIGS[3]
+    res = gpu_run(w, heads=[0, 29], want_stats=True, norm=1)
+    qb = sample_blocks(res["info"]["n_blocks"], 6, seed=7)
+    _full_check(res, label=f"{w.name} spectral", query_blocks=qb)
+
+
+# ---------------------------------------------------------------------------------------------
 # FLUX-like layer (24 heads, L = 4608, B = 64): every head's selection, four heads' outputs.
 # ---------------------------------------------------------------------------------------------
 

@@ -170,6 +170,37 @@ def test_global_minus_block_first_order_closed_form():
             assert np.max(np.abs((g["out"][t] - b["out"][t]) - corr / D)) < 1e-12
 
 
+# --- spectral reading of M_j: power iteration on tiny blocks, rank-1 and norm-ordering checks -------
+
+@pytest.mark.parametrize("L,d,B,keep", CASES)
+def test_spectral_m_matches_power_iteration(L, d, B, keep):
+    q, k, v = _rand(L, d, seed=5 * L + 3)
+    tau = 1 / math.sqrt(d)
+    st = po.head_stats(q, k, v, B, tau, norm="spectral")
+    fro = po.head_stats(q, k, v, B, tau).M
+    bs = brute.block_stats(*_lists(q, k, v), B, tau)
+    for j in range(len(st.n)):
+        E = [[bs["H"][j][a][b] - bs["Hbar"][a][b] for b in range(d)] for a in range(d)]
+        assert abs(st.M[j] - brute.spectral_norm(E)) <= 1e-9 * max(1.0, fro[j])
+        assert st.M[j] <= fro[j] * (1 + 1e-12) and fro[j] <= math.sqrt(d) * st.M[j] * (1 + 1e-12)
+
+
+def test_spectral_equals_frobenius_for_rank_one():
+    # one key direction per block and H-bar = 0 make every H_j - H-bar rank one
+    L, d, B = 64, 6, 8
+    rng = np.random.default_rng(17)
+    dirn = rng.standard_normal(d)
+    k = np.outer(rng.standard_normal(L), dirn)
+    k -= np.repeat(k.reshape(-1, B, d).mean(axis=1), B, axis=0)  # zero-mean blocks: H_j = K_j^T V_j
+    v = rng.standard_normal((L, d))
+    v[L // 2:] = -v[:L // 2][::-1]  # ... and K_j^T V_j of mirrored halves cancel in H-bar
+    k[L // 2:] = k[:L // 2][::-1]
+    st_s = po.head_stats(rng.standard_normal((L, d)), k, v, B, 1.0, norm="spectral")
+    st_f = po.head_stats(rng.standard_normal((L, d)), k, v, B, 1.0)
+    assert np.max(np.abs(st_f.Hbar)) < 1e-12
+    assert np.allclose(st_s.M, st_f.M, rtol=1e-12, atol=1e-12)
+
+
 # --- P6: H-bar identity from whole-matrix products ------------------------------------------------
 
 def test_hbar_identity():
