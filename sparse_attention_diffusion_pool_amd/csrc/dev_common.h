@@ -41,7 +41,32 @@ __device__ __forceinline__ void buf_load_lds16(__amdgpu_buffer_rsrc_t r, void* l
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, 0, 0, 0);
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima), through the builtin so that the
+// compiler's wait-count bookkeeping knows every earlier vector-memory load has completed.
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// The same direct copy (16 bytes per lane, lane l's bytes at lds_base + soff_lds + 16 l, global
+// offset voff + soff), issued from inline assembly. The compiler's wait-count insertion cannot tell
+// direct-to-LDS copies into one buffer from reads of another, so after a copy issued through the
+// builtin it makes every later LDS read wait for the copy; from assembly it does not see the copy
+// at all, and the caller waits for completion itself (wait_vmem) before reading the destination.
+// The instruction has no register results; its address operands are read when it issues.
+__device__ __forceinline__ void buf_load_lds16_async(const u32x4& rsrc, void* lds_base, uint32_t voff, uint32_t soff) {
+  const uint32_t m0v = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_base;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
+// Buffer resource words for buf_load_lds16_async (same format as make_rsrc).
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, kRsrcWord3};
+}
 
 __device__ __forceinline__ i16x4 lds_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
@@ -109,6 +134,17 @@ __device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t r, char* lds, u
                                              (NWAVES == 2 ? (m & ~1) : m) * NWAVES * 1024, 0, 0);
 }
 
+// copy_tile through buf_load_lds16_async (rsrc from rsrc_words).
+template <int ROWS, int NWAVES>
+__device__ __forceinline__ void copy_tile_async(const u32x4& r, char* lds, uint32_t vbase, int wave,
+                                                uint32_t vbase2 = 0) {
+  static_assert((NWAVES % 4 == 0 || NWAVES == 2) && ROWS % (4 * NWAVES) == 0, "copy_tile layout");
+#pragma unroll
+  for (int m = 0; m < ROWS / 4 / NWAVES; ++m)
+    buf_load_lds16_async(r, lds + 1024 * (m * NWAVES + wave), (NWAVES == 2 && (m & 1)) ? vbase2 : vbase,
+                         (NWAVES == 2 ? (m & ~1) : m) * NWAVES * 1024);
+}
+
 // extra_rows: 0, or 8 for the odd instructions of a 2-wave copy
 template <bool TR>
 __device__ __forceinline__ uint32_t copy_vbase(int wave, int lane, int extra_rows = 0) {
@@ -140,6 +176,13 @@ __device__ __forceinline__ bf16x8 tr_operand(const char* tile, uint32_t key_lo, 
   i16x4 a = lds_tr16(tr_addr(tile, key_lo + dr, c0 + dc));
   i16x4 b = lds_tr16(tr_addr(tile, key_hi + dr, c0 + dc));
   return join_tr(a, b);
+}
+
+// max(x[l], x[l ^ 32]) in every lane, through v_permlane32_swap (no LDS round trip): the swap of
+// x with itself hands each lane the other half's value in one of the two results.
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
