@@ -55,10 +55,15 @@ __device__ __forceinline__ void wait_vmem() {
 // at all, and the caller waits for completion itself (wait_vmem) before reading the destination.
 // The instruction has no register results; its address operands are read when it issues.
 __device__ __forceinline__ void buf_load_lds16_async(const u32x4& rsrc, void* lds_base, uint32_t voff, uint32_t soff) {
-  const uint32_t m0v = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_base;
+  // the LDS base, the resource and the scalar offset are wave-uniform: pin them to SGPRs
+  const uint32_t m0v =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_base);
+  const u32x4 r = {(uint32_t)__builtin_amdgcn_readfirstlane(rsrc[0]), (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[1]),
+                   (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[2]), (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[3])};
+  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff)
+               : "s"(m0v), "v"(voff), "s"(r), "s"(so)
                : "memory", "m0");
 }
 
