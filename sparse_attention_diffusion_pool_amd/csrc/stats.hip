@@ -326,7 +326,8 @@ __device__ float spectral_norm(SpecLds<D>& S, int tid) {
   return sqrtf(0.5f * (S.lo_hi[0] + S.lo_hi[1]));
 }
 
-template <int BLK, bool SPEC>
+// SPEC: spectral-norm M_j; HJT: also store H_j^T in bf16 (block-wise first-order variant)
+template <int BLK, bool SPEC, bool HJT>
 __global__ __launch_bounds__(256) void stats_cov_bf16(Dims dm, Work w, const __bf16* __restrict__ K,
                                                       const __bf16* __restrict__ V) {
   __shared__ __attribute__((aligned(1024))) char Ks[BLK * 256];
@@ -349,9 +350,8 @@ __global__ __launch_bounds__(256) void stats_cov_bf16(Dims dm, Work w, const __b
   const float* vs = w.vsum + ((size_t)h * dm.Nb + j) * 128;
   const float* hb = w.hbar + (size_t)h * 128 * 128;
   float ss = 0.f;
-  // block-wise first-order variant: keep H_j^T in bf16 (row b holds H_j[:, b])
-  __bf16* hjt = block_first_order(dm) ? reinterpret_cast<__bf16*>(w.hjT_lo) + ((size_t)h * dm.Nb + j) * 128 * 128
-                                      : nullptr;
+  // H_j^T in bf16 for the block-wise first-order variant (row b holds H_j[:, b])
+  __bf16* hjt = reinterpret_cast<__bf16*>(w.hjT_lo) + ((size_t)h * dm.Nb + j) * 128 * 128;
   for (int ct = 0; ct < 4; ++ct) {
     const int b = 32 * ct + l32;
     const float vb = vs[b];
@@ -363,10 +363,10 @@ __global__ __launch_bounds__(256) void stats_cov_bf16(Dims dm, Work w, const __b
         const float h_ab = acc[ct][x] - kb[a] * vb;
         const float hv = h_ab - hb[a * 128 + b];
         ss += hv * hv;
-        hj[r] = (__bf16)h_ab;
+        if constexpr (HJT) hj[r] = (__bf16)h_ab;
         if constexpr (SPEC) spec.E[a][b] = hv;
       }
-      if (hjt != nullptr) *reinterpret_cast<bf16x4*>(hjt + b * 128 + 32 * wave + 8 * g + 4 * hh) = hj;
+      if constexpr (HJT) *reinterpret_cast<bf16x4*>(hjt + b * 128 + 32 * wave + 8 * g + 4 * hh) = hj;
     }
   }
   if constexpr (SPEC) {
@@ -542,17 +542,23 @@ hipError_t launch_stats_cov_bf16(const Dims& dm, const Work& w, const void* K, c
   dim3 grid(dm.Nb, dm.H);
   auto k = static_cast<const __bf16*>(K);
   auto v = static_cast<const __bf16*>(V);
-  if (dm.spectral) {
-    if (dm.B == 128)
-      hipLaunchKernelGGL((stats_cov_bf16<128, true>), grid, dim3(256), 0, s, dm, w, k, v);
-    else
-      hipLaunchKernelGGL((stats_cov_bf16<64, true>), grid, dim3(256), 0, s, dm, w, k, v);
+#define PISA_COV(BLK, SPEC, HJT) \
+  hipLaunchKernelGGL((stats_cov_bf16<BLK, SPEC, HJT>), grid, dim3(256), 0, s, dm, w, k, v)
+  const bool hjt = block_first_order(dm);
+  if (dm.B == 128) {
+    if (dm.spectral) {
+      if (hjt) PISA_COV(128, true, true); else PISA_COV(128, true, false);
+    } else {
+      if (hjt) PISA_COV(128, false, true); else PISA_COV(128, false, false);
+    }
   } else {
-    if (dm.B == 128)
-      hipLaunchKernelGGL((stats_cov_bf16<128, false>), grid, dim3(256), 0, s, dm, w, k, v);
-    else
-      hipLaunchKernelGGL((stats_cov_bf16<64, false>), grid, dim3(256), 0, s, dm, w, k, v);
+    if (dm.spectral) {
+      if (hjt) PISA_COV(64, true, true); else PISA_COV(64, true, false);
+    } else {
+      if (hjt) PISA_COV(64, false, true); else PISA_COV(64, false, false);
+    }
   }
+#undef PISA_COV
   return hipGetLastError();
 }
 
