@@ -57,35 +57,60 @@ __device__ __forceinline__ LaneOffsets lane_offsets(uint32_t lane) {
 
 // S^T for NT key subtiles of 32 rows starting at row r0 (r0 % 16 == 0):
 // S[t] = Tile[r0 + 32 t + l32][:] . Q^T
+// The K-row reads run two d-chunks ahead of the MFMAs that use them, through an explicit ring of
+// operand registers; the scheduling fences keep the compiler from sinking each read next to its
+// MFMA (which would expose one LDS round trip per MFMA).
 template <int NT>
 __device__ __forceinline__ void qk_tile(const char* tile, uint32_t r0, const bf16x8 qreg[8], f32x16 S[NT],
                                         const LaneOffsets& lo) {
+  constexpr int kAhead = 2, kRing = kAhead + 1;
+  bf16x8 a[kRing][NT];
+  auto load = [&](int s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      a[s % kRing][t] = *reinterpret_cast<const bf16x8*>(tile + (r0 + 32 * t) * 256 + lo.krd[s]);
+  };
 #pragma unroll
   for (int t = 0; t < NT; ++t) S[t] = f32x16{};
 #pragma unroll
-  for (int s = 0; s < 8; ++s)
+  for (int s = 0; s < kAhead; ++s) load(s);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(tile + (r0 + 32 * t) * 256 + lo.krd[s]);
-      S[t] = mfma32(a, qreg[s], S[t]);
-    }
+  for (int s = 0; s < 8; ++s) {
+    if (s + kAhead < 8) load(s + kAhead);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) S[t] = mfma32(a[s % kRing][t], qreg[s], S[t]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
-// O^T[dt] += V^T P^T over NT key subtiles starting at key r0 (r0 % 4 == 0).
+// O^T[dt] += V^T P^T over NT key subtiles starting at key r0 (r0 % 4 == 0). MFMA groups are
+// (dt, t) in that order; the transpose reads of a group are issued two groups ahead.
 template <int NT>
 __device__ __forceinline__ void pv_tile(const char* Vs, uint32_t r0, const bf16x8 P[NT][2], f32x16 O[4],
                                         const LaneOffsets& lo) {
+  constexpr int kGroups = 4 * NT, kAhead = 2, kRing = kAhead + 1;
+  i16x4 x[kRing][2], y[kRing][2];
+  auto load = [&](int g) __attribute__((always_inline)) {
+    const int dt = g / NT, t = g % NT;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+    for (int u = 0; u < 2; ++u) {
+      const char* base = Vs + (r0 + 32 * t + 16 * u) * 256 + lo.vrd[dt];
+      x[g % kRing][u] = lds_tr16(base);
+      y[g % kRing][u] = lds_tr16(base + 8 * 256);
+    }
+  };
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+  for (int g = 0; g < kAhead; ++g) load(g);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const char* base = Vs + (r0 + 32 * t + 16 * u) * 256 + lo.vrd[dt];
-        const i16x4 x = lds_tr16(base);
-        const i16x4 y = lds_tr16(base + 8 * 256);
-        O[dt] = mfma32(join_tr(x, y), P[t][u], O[dt]);
-      }
+  for (int g = 0; g < kGroups; ++g) {
+    if (g + kAhead < kGroups) load(g + kAhead);
+    __builtin_amdgcn_sched_barrier(0);
+    const int dt = g / NT, t = g % NT;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) O[dt] = mfma32(join_tr(x[g % kRing][u], y[g % kRing][u]), P[t][u], O[dt]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // Workgroup id -> work item. Workgroup ids go to the 8 XCDs round-robin and start roughly in id
