@@ -309,9 +309,20 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
           } else {
             p = __builtin_amdgcn_exp2f(fmaf(Sc[u][x], cs, -mref));
           }
-          lsum += p;
+          if constexpr (KIND == 2) lsum += p;
           P[u][v][e] = (__bf16)p;
         }
+    if constexpr (KIND != 2) {
+      // row sum of the rounded probabilities (those the numerator's MFMA uses), two per dot2
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+      for (int u = 0; u < NT; ++u)
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P[u][v][2 * e], P[u][v][2 * e + 1]}, ones, lsum, false);
+    }
     pv_tile<NT>(ST ? sV1 : sV0, 0, P, O, lofs);
   };
 
