@@ -249,16 +249,21 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
     bf16x8 P[NT][2];
     qk_tile<NT>(ST ? sK1 : sK0, 0, qreg, Sc, lofs);
     float mx = -INFINITY;
+    // pooled token of this lane's element c = 0 (element x adds 32 u + 8 (x >> 2) + (x & 3)); made
+    // opaque per step so that the per-element constants are not hoisted out of the step loop,
+    // where they would pin about 32 registers and force spills
+    int jb = (s - E) * kKT + 4 * (int)hh;
+    if constexpr (KIND == 2) asm volatile("" : "+v"(jb));
     if constexpr (KIND == 2) {
       const int key_base = (s - E) * kKT;  // pooled token index of the step's first key
 #pragma unroll
       for (int u = 0; u < NT; ++u) {
-        const uint32_t word = selm[(key_base + 32 * u) / 32];
+        const uint32_t word = selm[(key_base + 32 * u) / 32] >> (4 * hh);
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
-          const int kin = 8 * (x >> 2) + 4 * hh + (x & 3);
-          const int j = key_base + 32 * u + kin;
-          const bool ok = j < Nb && !((word >> kin) & 1u);
+          const int c = 8 * (x >> 2) + (x & 3);
+          const int j = jb + 32 * u + c;
+          const bool ok = j < Nb && !((word >> c) & 1u);
           const float lg = ok ? (j == Nb - 1 ? lgLast : lgB) : -INFINITY;
           Sc[u][x] = fmaf(Sc[u][x], cs, lg);
           mx = fmaxf(mx, Sc[u][x]);
@@ -303,7 +308,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
           const int x = 8 * v + e;
           float p;
           if constexpr (KIND == 2) {
-            const int j = (s - E) * kKT + 32 * u + 8 * (x >> 2) + 4 * hh + (x & 3);
+            const int j = jb + 32 * u + 8 * (x >> 2) + (x & 3);
             p = __builtin_amdgcn_exp2f(Sc[u][x] - mref);
             beta = fmaf(p, j == Nb - 1 ? invLast : invB, beta);
           } else {
