@@ -35,7 +35,8 @@ __global__ __launch_bounds__(256) void route_kernel(Dims dm, Work w) {
   const float* kbar = w.kbar + (size_t)h * Nb * D;
   const float* M = w.M + (size_t)h * Nb;
 
-  for (int e = tid; e < kRows * D; e += 256) {
+#pragma unroll
+  for (int e = tid; e < kRows * D; e += 256) {  // all loads in flight at once
     const int r = e / D, c = e % D;
     qs[r][c] = (i0 + r < Nb) ? qbar[(size_t)(i0 + r) * D + c] : 0.f;
   }
@@ -46,25 +47,51 @@ __global__ __launch_bounds__(256) void route_kernel(Dims dm, Work w) {
     qn[tid] = sqrtf(s);
   }
 
+  // key[][] is indexed with compile-time indices only (every loop over it is unrolled), so that it
+  // stays in registers
   uint32_t key[kRowsPerWave][NS];
+  // The next centroid tile (this thread's share, and M_j of the lane's key) is loaded into
+  // registers while the current one is used, so one tile's load latency overlaps the previous
+  // tile's dot products instead of adding up load by load.
+  constexpr int kPer = 64 * (D / 4) / 256;  // 16-byte pieces of a tile per thread
+  f32x4 pre[kPer];
+  float mpre = 0.f;
+  auto fetch = [&](int jt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < kPer; ++it) {
+      const int e = tid + 256 * it;
+      const int r = e / (D / 4), c4 = e % (D / 4);
+      pre[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (jt + r < Nb) pre[it] = *reinterpret_cast<const f32x4*>(kbar + (size_t)(jt + r) * D + 4 * c4);
+    }
+    mpre = (jt + lane < Nb) ? M[jt + lane] : 0.f;
+  };
+  fetch(0);
+#pragma unroll
   for (int s = 0; s < NS; ++s) {
     __syncthreads();  // previous tile consumed (and qn visible on the first pass)
     const int jt = 64 * s;
+    float mj = 0.f;
     if (jt < Nb) {
-      for (int e = tid; e < 64 * (D / 4); e += 256) {
+#pragma unroll
+      for (int it = 0; it < kPer; ++it) {
+        const int e = tid + 256 * it;
         const int r = e / (D / 4), c4 = e % (D / 4);
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (jt + r < Nb) v = *reinterpret_cast<const f32x4*>(kbar + (size_t)(jt + r) * D + 4 * c4);
-        *reinterpret_cast<f32x4*>(&kt[r][4 * c4]) = v;
+        *reinterpret_cast<f32x4*>(&kt[r][4 * c4]) = pre[it];
       }
+      mj = mpre;
+      if (jt + 64 < Nb) fetch(jt + 64);
     }
     __syncthreads();
     const int j = jt + lane;
     float acc[kRowsPerWave];
+#pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r) acc[r] = 0.f;
     if (jt < Nb) {
+#pragma unroll 4
       for (int c4 = 0; c4 < D / 4; ++c4) {
         const f32x4 kv = *reinterpret_cast<const f32x4*>(&kt[lane][4 * c4]);
+#pragma unroll
         for (int r = 0; r < kRowsPerWave; ++r) {
           const f32x4 qv = *reinterpret_cast<const f32x4*>(&qs[kRowsPerWave * wave + r][4 * c4]);
           acc[r] = fmaf(qv[0], kv[0], acc[r]);
@@ -75,8 +102,8 @@ __global__ __launch_bounds__(256) void route_kernel(Dims dm, Work w) {
       }
     }
     const bool valid = j < Nb;
-    const float mj = valid ? M[j] : 0.f;
     const float nj = (j == Nb - 1) ? (float)dm.n_last : (float)dm.B;
+#pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r) {
       float sc = acc[r];
       if (dm.routing == 0) sc += logf(fmaf(qn[kRowsPerWave * wave + r], mj, nj));
@@ -86,6 +113,7 @@ __global__ __launch_bounds__(256) void route_kernel(Dims dm, Work w) {
 
   const uint64_t ltmask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int kk = dm.k;
+#pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) {
     const int i = i0 + kRowsPerWave * wave + r;
     if (i >= Nb) break;  // uniform per wave
@@ -93,14 +121,17 @@ __global__ __launch_bounds__(256) void route_kernel(Dims dm, Work w) {
     for (int b = 31; b >= 0; --b) {
       const uint32_t cand = T | (1u << b);
       int cnt = 0;
+#pragma unroll
       for (int s = 0; s < NS; ++s) cnt += __popcll(__ballot(key[r][s] >= cand));
       if (cnt >= kk) T = cand;
     }
     int gt = 0;
+#pragma unroll
     for (int s = 0; s < NS; ++s) gt += __popcll(__ballot(key[r][s] > T));
     const int need = kk - gt;
     int eq_seen = 0, base = 0;
     int32_t* out = w.idx + ((size_t)h * Nb + i) * kk;
+#pragma unroll
     for (int s = 0; s < NS; ++s) {
       const bool eq = key[r][s] == T;
       const uint64_t eqm = __ballot(eq);
