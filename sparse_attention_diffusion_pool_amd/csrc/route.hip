@@ -88,7 +88,6 @@ __global__ __launch_bounds__(256) void route_kernel(Dims dm, Work w) {
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r) acc[r] = 0.f;
     if (jt < Nb) {
-#pragma unroll 4
       for (int c4 = 0; c4 < D / 4; ++c4) {
         const f32x4 kv = *reinterpret_cast<const f32x4*>(&kt[lane][4 * c4]);
 #pragma unroll
