@@ -206,15 +206,15 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
       const int n_j = (j == Nb - 1) ? dm.n_last : B;
       const size_t g0 = head + ((size_t)j * B + r0) * 128;
       const uint32_t bytes = (uint32_t)(n_j - r0) * 256;  // rows past the block end read as zero
-      copy_tile_async<kKT, NW>(rsrc_words(K + g0, bytes), Ks, vb_row, wave, vb_row2);
-      copy_tile_async<kKT, NW>(rsrc_words(V + g0, bytes), Vs, vb_tr, wave, vb_tr2);
+      copy_tile_async<kKT, NW>(rsrc_words(K + g0, bytes), lds_addr(Ks), vb_row, wave, vb_row2);
+      copy_tile_async<kKT, NW>(rsrc_words(V + g0, bytes), lds_addr(Vs), vb_tr, wave, vb_tr2);
     } else if (s < S_main) {
       const size_t g0 = (size_t)(s - E) * kKT * 128;
-      copy_tile_async<kKT, NW>(rsrc_words(kl + g0, kKT * 256), Ks, vb_row, wave, vb_row2);
-      copy_tile_async<kKT, NW>(rsrc_words(vl + g0, kKT * 256), Vs, vb_tr, wave, vb_tr2);
+      copy_tile_async<kKT, NW>(rsrc_words(kl + g0, kKT * 256), lds_addr(Ks), vb_row, wave, vb_row2);
+      copy_tile_async<kKT, NW>(rsrc_words(vl + g0, kKT * 256), lds_addr(Vs), vb_tr, wave, vb_tr2);
     } else {
-      copy_tile_async<kKT, NW>(rsrc_words(ht, kKT * 256), Ks, vb_row, wave, vb_row2);
-      copy_tile_async<kKT, NW>(rsrc_words(ht + kKT * 128, kKT * 256), Vs, vb_row, wave, vb_row2);
+      copy_tile_async<kKT, NW>(rsrc_words(ht, kKT * 256), lds_addr(Ks), vb_row, wave, vb_row2);
+      copy_tile_async<kKT, NW>(rsrc_words(ht + kKT * 128, kKT * 256), lds_addr(Vs), vb_row, wave, vb_row2);
     }
   };
   issue(0, Stage<0>{});

@@ -55,10 +55,10 @@ __device__ __forceinline__ void wait_vmem() {
 // builtin it makes every later LDS read wait for the copy; from assembly it does not see the copy
 // at all, and the caller waits for completion itself (wait_vmem) before reading the destination.
 // The instruction has no register results; its address operands are read when it issues.
-__device__ __forceinline__ void buf_load_lds16_async(const u32x4& rsrc, void* lds_base, uint32_t voff, uint32_t soff) {
+// lds_base is an LDS byte address (lds_addr of a __shared__ object plus an offset).
+__device__ __forceinline__ void buf_load_lds16_async(const u32x4& rsrc, uint32_t lds_base, uint32_t voff, uint32_t soff) {
   // the LDS base, the resource and the scalar offset are wave-uniform: pin them to SGPRs
-  const uint32_t m0v =
-      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_base);
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
   const u32x4 r = {(uint32_t)__builtin_amdgcn_readfirstlane(rsrc[0]), (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[1]),
                    (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[2]), (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[3])};
   const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
@@ -66,6 +66,13 @@ __device__ __forceinline__ void buf_load_lds16_async(const u32x4& rsrc, void* ld
                :
                : "s"(m0v), "v"(voff), "s"(r), "s"(so)
                : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ object. Applied to the object itself it folds to a constant;
+// kept as a 32-bit address afterwards, the copies need no generic-to-LDS pointer conversion
+// (with its null check) per instruction.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
 // Buffer resource words for buf_load_lds16_async (same format as make_rsrc).
@@ -142,12 +149,12 @@ __device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t r, char* lds, u
 
 // copy_tile through buf_load_lds16_async (rsrc from rsrc_words).
 template <int ROWS, int NWAVES>
-__device__ __forceinline__ void copy_tile_async(const u32x4& r, char* lds, uint32_t vbase, int wave,
+__device__ __forceinline__ void copy_tile_async(const u32x4& r, uint32_t lds, uint32_t vbase, int wave,
                                                 uint32_t vbase2 = 0) {
   static_assert((NWAVES % 4 == 0 || NWAVES == 2) && ROWS % (4 * NWAVES) == 0, "copy_tile layout");
 #pragma unroll
   for (int m = 0; m < ROWS / 4 / NWAVES; ++m)
-    buf_load_lds16_async(r, lds + 1024 * (m * NWAVES + wave), (NWAVES == 2 && (m & 1)) ? vbase2 : vbase,
+    buf_load_lds16_async(r, lds + 1024u * (m * NWAVES + wave), (NWAVES == 2 && (m & 1)) ? vbase2 : vbase,
                          (NWAVES == 2 ? (m & ~1) : m) * NWAVES * 1024);
 }
 
