@@ -176,6 +176,28 @@ def time_stages(plan, qd, kd, vd, out, stream, steps, warmup):
     return t
 
 
+def mfma_probe(dev, blocks: int = 2048, iters: int = 2000) -> dict:
+    """The MFMA throughput and shader clock the chip sustains on a pure loop of the attention
+    kernel's MFMA instruction (pisa_debug_mfma_probe): 8 workgroups of 4 waves per CU."""
+    import torch
+    from sparse_attention_diffusion_pool_amd import _lib as L
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    clk = torch.empty(blocks * 2, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream()
+    L.mfma_probe(out, clk, blocks, iters, stream)  # warm-up (clock ramp, code load)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    L.mfma_probe(out, clk, blocks, iters, stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    c = clk.view(blocks, 2).cpu().numpy().astype(np.float64)
+    flops = blocks * 4 * 4 * iters * 32768.0
+    return {"tflops": round(flops / (ms * 1e-3) / 1e12, 1), "ms": round(ms, 4),
+            "sclk_ghz": round(float(c[:, 0].sum() / c[:, 1].sum()) * 0.1, 3),
+            "loop": f"{blocks} workgroups x 4 waves x {iters} x 4 independent v_mfma_f32_32x32x16_bf16"}
+
+
 def selection_of(plan, info, H, dev):
     import torch
     idx = torch.empty((H, info["n_blocks"], info["k"]), dtype=torch.int32, device=dev)
@@ -479,6 +501,12 @@ def main():
                      "achieved": round(attend_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(attend_tflops / peak, 4), "traffic": traffic},
     }
+
+    if w.dtype == "bf16":
+        # measured MFMA ceiling on this machine, beside the spec peak of the roofline object
+        mp = mfma_probe(dev)
+        mp["attend_frac"] = round(attend_tflops / mp["tflops"], 4)
+        res["mfma_probe"] = mp
 
     if not args.no_quality:
         # quality check on sampled query blocks of 2 heads: relative L2 of PISA (this run's output)

@@ -151,6 +151,16 @@ pisa_status pisa_debug_copy_stats(pisa_plan_t *plan, float *qbar, float *kbar, f
 /* Test support: copy the selection: idx [H, N_b, k] int32, ascending block indices per row. */
 pisa_status pisa_debug_copy_selection(pisa_plan_t *plan, int32_t *idx, hipStream_t stream);
 
+/* Measurement support (no plan): `blocks` workgroups of 4 waves each run `iters` rounds of four
+ * independent v_mfma_f32_32x32x16_bf16 on register operands, the instruction the attention
+ * kernel is built on; FLOPs = blocks * 4 * 4 * iters * 32768. It gives the MFMA throughput and
+ * shader clock the chip sustains under a pure MFMA load (the spec peak assumes 2.4 GHz).
+ * out: device, blocks * 256 floats (results, kept live). clk: device, 2 * blocks uint64 per
+ * workgroup: shader-clock ticks (s_memtime) and constant 100 MHz ticks (s_memrealtime) over the
+ * loop. Asynchronous on `stream`. blocks in [1, 65536], iters in [1, 2^20], else
+ * PISA_ERR_INVALID_ARGUMENT; a failed launch gives PISA_ERR_DEVICE. */
+pisa_status pisa_debug_mfma_probe(int32_t blocks, int32_t iters, float *out, uint64_t *clk, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -58,6 +58,7 @@ _SIGS = {
     "pisa_last_error": (ctypes.c_char_p, []),
     "pisa_debug_copy_stats": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "pisa_debug_copy_selection": (ctypes.c_int, [_P, _P, _P]),
+    "pisa_debug_mfma_probe": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
 }
 
 _lib = None
@@ -198,3 +199,9 @@ def pisa_attention(Q, K, V, B: int, keep: float, routing=None, phases=None, scal
     out = torch.empty_like(Q)
     plan.forward(Q, K, V, out, stream)
     return out, plan
+
+
+def mfma_probe(out, clk, blocks: int, iters: int, stream=None) -> None:
+    """pisa_debug_mfma_probe: out float32 [blocks * 256], clk int64 [blocks * 2] (device tensors)."""
+    check(load().pisa_debug_mfma_probe(int(blocks), int(iters), _ptr(out), _ptr(clk), _stream(stream)),
+          "pisa_debug_mfma_probe")

@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libpisa.so")
-SOURCES = ["pisa_host.cpp", "stats.hip", "route.hip", "attend_bf16.hip", "attend_f32.hip"]
+SOURCES = ["pisa_host.cpp", "stats.hip", "route.hip", "attend_bf16.hip", "attend_f32.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -424,6 +424,15 @@ pisa_status pisa_debug_copy_selection(pisa_plan_t* p, int32_t* idx, hipStream_t 
   return PISA_OK;
 }
 
+pisa_status pisa_debug_mfma_probe(int32_t blocks, int32_t iters, float* out, uint64_t* clk, hipStream_t stream) {
+  if (blocks < 1 || blocks > 65536) return fail(PISA_ERR_INVALID_ARGUMENT, "blocks must be in [1, 65536], got %d", blocks);
+  if (iters < 1 || iters > (1 << 20)) return fail(PISA_ERR_INVALID_ARGUMENT, "iters must be in [1, 2^20], got %d", iters);
+  if (out == nullptr || clk == nullptr) return fail(PISA_ERR_INVALID_ARGUMENT, "out and clk must not be NULL");
+  pisa_status s = check_device();
+  if (s != PISA_OK) return s;
+  return launched(pisa::launch_mfma_probe(blocks, iters, out, clk, stream), "mfma probe");
+}
+
 }  // extern "C"
 
 namespace pisa {

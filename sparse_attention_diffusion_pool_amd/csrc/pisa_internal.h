@@ -74,6 +74,7 @@ hipError_t launch_stats_cov_bf16(const Dims&, const Work&, const void*, const vo
 hipError_t launch_stats_pass_f32(const Dims&, const Work&, const void*, const void*, const void*, hipStream_t);
 hipError_t launch_stats_cov_f32(const Dims&, const Work&, const void*, const void*, hipStream_t);
 hipError_t launch_attend_bf16(const Dims&, const Work&, const void*, const void*, const void*, void*, hipStream_t);
+hipError_t launch_mfma_probe(int blocks, int iters, float* out, uint64_t* clk, hipStream_t s);
 hipError_t launch_first_block_bf16(const Dims&, const Work&, const void*, void*, hipStream_t);
 hipError_t launch_attend_f32(const Dims&, const Work&, const void*, const void*, const void*, void*, hipStream_t);
 

@@ -143,7 +143,8 @@ def test_forward_without_device_reports_device_error(lib):
     assert lib.pisa_plan_attach_workspace(p.handle, 256 * 1000, p.info()["workspace_bytes"]) == 0
     for call in (lambda: lib.pisa_forward(p.handle, 1 << 20, 1 << 30, 1 << 31, 1 << 32, None),
                  lambda: lib.pisa_forward_route(p.handle, None),
-                 lambda: lib.pisa_debug_copy_selection(p.handle, 1 << 20, None)):
+                 lambda: lib.pisa_debug_copy_selection(p.handle, 1 << 20, None),
+                 lambda: lib.pisa_debug_mfma_probe(8, 10, 1 << 20, 1 << 21, None)):
         assert call() == 5
         assert "device" in L.last_error()
 
@@ -163,3 +164,15 @@ def test_status_strings(lib):
     for s, name in L.STATUS.items():
         assert lib.pisa_status_string(s).decode() == name
     assert lib.pisa_status_string(42).decode() == "PISA_ERR_UNKNOWN"
+
+
+def test_mfma_probe_argument_checks(lib):
+    # argument errors come before any device use
+    buf = ctypes.c_void_p(1 << 20)
+    assert lib.pisa_debug_mfma_probe(0, 10, buf, buf, None) == 1
+    assert lib.pisa_debug_mfma_probe(65537, 10, buf, buf, None) == 1
+    assert lib.pisa_debug_mfma_probe(1, 0, buf, buf, None) == 1
+    assert lib.pisa_debug_mfma_probe(1, (1 << 20) + 1, buf, buf, None) == 1
+    assert lib.pisa_debug_mfma_probe(1, 10, None, buf, None) == 1
+    assert lib.pisa_debug_mfma_probe(1, 10, buf, None, None) == 1
+    assert "NULL" in L.last_error()

@@ -190,3 +190,24 @@ def test_outputs_untouched_outside_rows_and_no_nan():
     w = custom("fill", 2, (7, 11, 13), 128, 128, 0.3, "bf16")
     res = gpu_run(w)
     assert torch.isfinite(res["out"].float()).all()
+
+
+# ---------------------------------------------------------------------------------------------
+# Measurement support: the MFMA probe runs, its results are finite and its clock reading sane.
+# ---------------------------------------------------------------------------------------------
+
+def test_mfma_probe():
+    from sparse_attention_diffusion_pool_amd import _lib as L
+    blocks, iters = 256, 200
+    dev = torch.device("cuda", 0)
+    out = torch.full((blocks * 256,), float("nan"), dtype=torch.float32, device=dev)
+    clk = torch.zeros(blocks * 2, dtype=torch.int64, device=dev)
+    L.mfma_probe(out, clk, blocks, iters)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    assert np.isfinite(o).all() and (o > 0).all()
+    c = clk.view(blocks, 2).cpu().numpy().astype(np.float64)
+    assert (c > 0).all()
+    ghz = c[:, 0].sum() / c[:, 1].sum() * 0.1  # shader ticks per 100 MHz tick
+    log(f"[probe] shader clock {ghz:.3f} GHz over {blocks} workgroups")
+    assert 0.5 < ghz < 3.0
