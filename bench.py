@@ -91,7 +91,7 @@ def cpu_baseline(w, heads, sample_note):
             "sample": sample_note, "seconds": secs, "cpu": platform.processor() or platform.machine()}
 
 
-KERNELS = ("stats_pass_bf16", "stats_cov_bf16", "stats_finalize", "stats_f32", "route_kernel", "attend_bf16",
+KERNELS = ("stats_pass_bf16", "stats_cov_bf16", "stats_finalize", "stats_f32", "route_kernel", "attend_bf16", "mfma_probe",
            "attend_f32", "copyBuffer", "Fill")
 
 
