@@ -58,6 +58,7 @@ SMALL = [
     ("bf16-exact-multiple", 2, (16, 16), 0, 128, 128, 0.5, "bf16"),
     ("bf16-B64-text", 3, (20, 30), 100, 128, 64, 0.25, "bf16"),
     ("bf16-k1", 1, (20, 20, 10), 0, 128, 64, 0.01, "bf16"),
+    ("bf16-B64-short-tail", 2, (13, 10), 0, 128, 64, 0.5, "bf16"),
     ("bf16-dense", 2, (9, 10, 11), 0, 128, 128, 1.0, "bf16"),
     ("bf16-L-lt-B", 2, (5, 7), 0, 128, 128, 0.5, "bf16"),
     ("bf16-two-pooled-tiles", 2, (9, 30, 65), 0, 128, 128, 0.1, "bf16"),
@@ -76,12 +77,13 @@ def test_small_layers(case):
     _full_check(res, label=name)
 
 
+@pytest.mark.parametrize("B", [128, 64])
 @pytest.mark.parametrize("phases", [3, 1])
 @pytest.mark.parametrize("routing", [0, 1])
-def test_small_bf16_modes(phases, routing):
-    w = custom("bf16-modes", 2, (7, 11, 13), 128, 128, 0.3, "bf16")
+def test_small_bf16_modes(phases, routing, B):
+    w = custom("bf16-modes", 2, (7, 11, 13), 128, B, 0.3, "bf16")
     res = gpu_run(w, routing=routing, phases=phases)
-    _full_check(res, label=f"bf16 modes routing={routing} phases={phases}")
+    _full_check(res, label=f"bf16 modes B={B} routing={routing} phases={phases}")
 
 
 # ---------------------------------------------------------------------------------------------
