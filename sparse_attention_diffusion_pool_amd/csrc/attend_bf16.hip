@@ -32,6 +32,14 @@ namespace {
 constexpr int kMaskWords = (8192 + 128) / 32;  // N_b <= 8192, rounded up to a tile
 constexpr float kLazy = 8.0f;                   // rescale threshold (log2 units)
 
+// x rounded to a bf16 value >= x (finite x): the softmax reference must be exact in bf16 (it enters
+// an MFMA operand) and must not fall below the running max (p <= 2^kLazy).
+__device__ __forceinline__ float bf16_ceil(float x) {
+  uint32_t u = __float_as_uint(x);
+  u = (x > 0.0f) ? ((u + 0xffffu) & 0xffff0000u) : (u & 0xffff0000u);
+  return __uint_as_float(u);
+}
+
 // Per-lane LDS read offsets, computed once (relative to a tile's first row r0, r0 % 16 == 0):
 //   krd[s]: 16-byte row read of row r0 + l32, d-chunk 2 s + hh (row-read swizzle)
 //   vrd[dt]: transpose read of rows r0 + 4 hh + l16/4, columns 32 dt + 16 g16 + 4 (l16 % 4)
@@ -60,7 +68,8 @@ __device__ __forceinline__ LaneOffsets lane_offsets(uint32_t lane) {
 // The K-row reads run two d-chunks ahead of the MFMAs that use them, through an explicit ring of
 // operand registers; the scheduling fences keep the compiler from sinking each read next to its
 // MFMA (which would expose one LDS round trip per MFMA).
-template <int NT>
+// With kAccumulate the products are added to S as the caller initialised it.
+template <int NT, bool kAccumulate = false>
 __device__ __forceinline__ void qk_tile(const char* tile, uint32_t r0, const bf16x8 qreg[8], f32x16 S[NT],
                                         const LaneOffsets& lo) {
   constexpr int kAhead = 2, kRing = kAhead + 1;
@@ -70,8 +79,10 @@ __device__ __forceinline__ void qk_tile(const char* tile, uint32_t r0, const bf1
     for (int t = 0; t < NT; ++t)
       a[s % kRing][t] = *reinterpret_cast<const bf16x8*>(tile + (r0 + 32 * t) * 256 + lo.krd[s]);
   };
+  if constexpr (!kAccumulate) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t) S[t] = f32x16{};
+    for (int t = 0; t < NT; ++t) S[t] = f32x16{};
+  }
 #pragma unroll
   for (int s = 0; s < kAhead; ++s) load(s);
 #pragma unroll
@@ -228,8 +239,15 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
     for (int s = 0; s < 8; ++s)
       qreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, row * 256 + (16 * s + 8 * hh) * 2));
   }
-
+  // Q pre-scaled by scale * log2 e (rounded to bf16): the MFMA then gives scores in log2 units
   const float cs = dm.scale * kLog2e;
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qreg[s][e] = (__bf16)((float)qreg[s][e] * cs);
+  // A operand of the shift MFMA: A[key][k] = (k == 0), so A x B adds row 0 of B to every key
+  bf16x8 shift_a = {};
+  shift_a[0] = (__bf16)(hh == 0 ? 1.0f : 0.0f);
   const float lgB = __log2f((float)B), lgLast = __log2f((float)dm.n_last);
   const float invB = 1.0f / (float)B, invLast = 1.0f / (float)dm.n_last;
   float m = -INFINITY, lsum = 0.f, beta = 0.f;
@@ -247,8 +265,16 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
     if (s + 1 < S_all) issue(s + 1, Stage<ST ^ 1>{});
     f32x16 Sc[NT];
     bf16x8 P[NT][2];
-    qk_tile<NT>(ST ? sK1 : sK0, 0, qreg, Sc, lofs);
-    float mx = -INFINITY;
+    // The accumulators start at -m (B row 0 holds -m of the lane's query; m is exact in bf16), so
+    // the MFMA returns the exponent argument cs q.k - m and the softmax needs no FMA per score.
+    // (A lane whose keys have all been masked so far still has m = -inf: its shift is 0.)
+    const float mref = m == -INFINITY ? 0.0f : m;
+    bf16x8 shift_b = {};
+    shift_b[0] = (__bf16)(hh == 0 ? -mref : 0.0f);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) Sc[t] = mfma32(shift_a, shift_b, f32x16{});
+    qk_tile<NT, true>(ST ? sK1 : sK0, 0, qreg, Sc, lofs);
+    float mx = -INFINITY;  // of the scores relative to mref
     // pooled token of this lane's element c = 0 (element x adds 32 u + 8 (x >> 2) + (x & 3)); made
     // opaque per step so that the per-element constants are not hoisted out of the step loop,
     // where they would pin about 32 registers and force spills
@@ -265,7 +291,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
           const int j = jb + 32 * u + c;
           const bool ok = j < Nb && !((word >> c) & 1u);
           const float lg = ok ? (j == Nb - 1 ? lgLast : lgB) : -INFINITY;
-          Sc[u][x] = fmaf(Sc[u][x], cs, lg);
+          Sc[u][x] += lg;
           mx = fmaxf(mx, Sc[u][x]);
         }
       }
@@ -284,21 +310,21 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
       for (int u = 0; u < NT; ++u)
 #pragma unroll
         for (int x = 0; x < 16; ++x) mx = fmaxf(mx, Sc[u][x]);
-      mx *= cs;  // cs > 0: max of the scaled scores
     }
     mx = xor32_max(mx);
-    const bool up = mx > m + kLazy;
+    const bool up = mx > (m == -INFINITY ? -INFINITY : kLazy);
     if (__builtin_expect(__ballot(up) != 0, 0)) {
-      const float m_new = up ? mx : m;
+      const float m_new = up ? bf16_ceil(mref + mx) : m;
       const float alpha = up ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;
+      const float shift = up ? m_new - mref : 0.0f;
       m = m_new;
       lsum *= alpha;
       beta *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) O[dt] *= alpha;
+#pragma unroll
+      for (int u = 0; u < NT; ++u) Sc[u] -= shift;
     }
-    // a lane whose keys have all been masked so far still has m = -inf: its p must be 0, not NaN
-    const float mref = m == -INFINITY ? 0.0f : m;
 #pragma unroll
     for (int u = 0; u < NT; ++u)
 #pragma unroll
@@ -309,10 +335,10 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
           float p;
           if constexpr (KIND == 2) {
             const int j = jb + 32 * u + 8 * (x >> 2) + (x & 3);
-            p = __builtin_amdgcn_exp2f(Sc[u][x] - mref);
+            p = __builtin_amdgcn_exp2f(Sc[u][x]);
             beta = fmaf(p, j == Nb - 1 ? invLast : invB, beta);
           } else {
-            p = __builtin_amdgcn_exp2f(fmaf(Sc[u][x], cs, -mref));
+            p = __builtin_amdgcn_exp2f(Sc[u][x]);
           }
           if constexpr (KIND == 2) lsum += p;
           P[u][v][e] = (__bf16)p;
@@ -359,7 +385,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
   // ---- phase 3: global first-order correction --------------------------------------------
   if (do_first) {
     f32x16 T2[2];
-    const float bt = beta * dm.scale;
+    const float bt = beta * (dm.scale / cs);  // q is pre-scaled by cs
     qk_tile<2>(hstage ? sK1 : sK0, 0, qreg, T2, lofs);  // H-bar^T rows 0..63
     O[0] += bt * T2[0];
     O[1] += bt * T2[1];
