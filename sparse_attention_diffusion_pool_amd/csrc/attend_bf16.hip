@@ -245,8 +245,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
   for (int s = 0; s < 8; ++s)
 #pragma unroll
     for (int e = 0; e < 8; ++e) qreg[s][e] = (__bf16)((float)qreg[s][e] * cs);
-  // A operand of the shift MFMA: A[key][k] = (k == 0), so A x B adds row 0 of B to every key
-  bf16x8 shift_a = {};
+  // A operand of the shift MFMA: A[key][k] = (k == 0), so A x B adds row 0 of B to every key.
+  // B: row 0 holds -m of the lane's query (0 while m = -inf); it changes only with m.
+  bf16x8 shift_a = {}, shift_b = {};
   shift_a[0] = (__bf16)(hh == 0 ? 1.0f : 0.0f);
   const float lgB = __log2f((float)B), lgLast = __log2f((float)dm.n_last);
   const float invB = 1.0f / (float)B, invLast = 1.0f / (float)dm.n_last;
@@ -265,12 +266,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
     if (s + 1 < S_all) issue(s + 1, Stage<ST ^ 1>{});
     f32x16 Sc[NT];
     bf16x8 P[NT][2];
-    // The accumulators start at -m (B row 0 holds -m of the lane's query; m is exact in bf16), so
-    // the MFMA returns the exponent argument cs q.k - m and the softmax needs no FMA per score.
-    // (A lane whose keys have all been masked so far still has m = -inf: its shift is 0.)
-    const float mref = m == -INFINITY ? 0.0f : m;
-    bf16x8 shift_b = {};
-    shift_b[0] = (__bf16)(hh == 0 ? -mref : 0.0f);
+    // The accumulators start at -m (m is exact in bf16), so the MFMA returns the exponent argument
+    // cs q.k - m and the softmax needs no FMA per score. (A lane whose keys have all been masked so
+    // far still has m = -inf: its shift is 0.)
 #pragma unroll
     for (int t = 0; t < NT; ++t) Sc[t] = mfma32(shift_a, shift_b, f32x16{});
     qk_tile<NT, true>(ST ? sK1 : sK0, 0, qreg, Sc, lofs);
@@ -314,10 +312,12 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
     mx = xor32_max(mx);
     const bool up = mx > (m == -INFINITY ? -INFINITY : kLazy);
     if (__builtin_expect(__ballot(up) != 0, 0)) {
+      const float mref = m == -INFINITY ? 0.0f : m;
       const float m_new = up ? bf16_ceil(mref + mx) : m;
       const float alpha = up ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;
       const float shift = up ? m_new - mref : 0.0f;
       m = m_new;
+      shift_b[0] = (__bf16)(hh == 0 && m != -INFINITY ? -m : 0.0f);
       lsum *= alpha;
       beta *= alpha;
 #pragma unroll
