@@ -111,6 +111,57 @@ def summarize_trace(d: str) -> None:
               f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
 
 
+# Counter passes for --summarize-counters (each within one rocprofv3 run's hardware limits:
+# at most 8 SQ, 4 TCC and 2 GRBM counters), collected together with --kernel-trace.
+COUNTER_PASSES = {
+    "p1": "GRBM_GUI_ACTIVE SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU "
+          "SQ_INSTS_LDS SQ_INSTS_SALU SQ_INSTS_VMEM",
+    "p2": "GRBM_GUI_ACTIVE SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS "
+          "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_ANY TCC_HIT_sum TCC_MISS_sum",
+}
+
+
+def summarize_counters(d: str) -> None:
+    """Per-kernel counter summary from the COUNTER_PASSES directories under d (rocprofv3 --kernel-trace
+    --pmc ... over the benchmark). Counters are averaged per dispatch. GRBM_GUI_ACTIVE is summed over
+    the 8 XCDs; SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs; SQ_WAVE_CYCLES and the SQ wait / active
+    counters count in units of 4 cycles per wave."""
+    import collections
+    import csv
+
+    vals = collections.defaultdict(dict)
+    durs = collections.defaultdict(list)
+    for sub in COUNTER_PASSES:
+        agg = collections.defaultdict(float)
+        disp = collections.defaultdict(set)
+        for r in csv.DictReader(open(os.path.join(d, sub, "run_counter_collection.csv"))):
+            k = short_kernel(r["Kernel_Name"])
+            agg[(k, r["Counter_Name"])] += float(r["Counter_Value"])
+            disp[k].add(r["Dispatch_Id"])
+        for (k, c), v in agg.items():
+            vals[k][c] = v / len(disp[k])
+        for r in csv.DictReader(open(os.path.join(d, sub, "run_kernel_trace.csv"))):
+            durs[short_kernel(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    print("| kernel | ms (under counters) | shader clock (GHz) | MFMA busy (of SIMD cycles) | "
+          "VALU / LDS / SALU / VMEM instr per MFMA | waves waiting (of wave time) | LDS bank conflicts "
+          "(of LDS-active cycles) | L2 hit rate |")
+    print("|---|---|---|---|---|---|---|---|")
+    for k in ("attend_bf16", "stats_pass_bf16", "stats_cov_bf16", "route_kernel", "stats_finalize", "mfma_probe"):
+        a = vals.get(k)
+        if not a or not durs.get(k):
+            continue
+        dur = sum(durs[k]) / len(durs[k])
+        cyc = a["GRBM_GUI_ACTIVE"] / 8
+        mf = a.get("SQ_INSTS_MFMA", 0.0)
+        mix = ("/".join(f"{a[c] / mf:.2f}" for c in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM"))
+               if mf > 0 else "-")
+        busy = a.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (cyc * 1024)
+        wait = a["SQ_WAIT_ANY"] / a["SQ_WAVE_CYCLES"] if a.get("SQ_WAVE_CYCLES") else float("nan")
+        bank = a["SQ_LDS_BANK_CONFLICT"] / a["SQ_LDS_IDX_ACTIVE"] if a.get("SQ_LDS_IDX_ACTIVE") else 0.0
+        hit = a["TCC_HIT_sum"] / max(a["TCC_HIT_sum"] + a["TCC_MISS_sum"], 1.0)
+        print(f"| {k} | {dur * 1e3:.3f} | {cyc / dur / 1e9:.2f} | {busy:.3f} | {mix} | {wait:.3f} | {bank:.4f} | {hit:.3f} |")
+
+
 def summarize_traffic(d: str, command: str) -> None:
     """HBM-side bytes per attention launch from two rocprofv3 --pmc passes (FETCH_SIZE, then
     WRITE_SIZE, KiB per dispatch) over the benchmark, each scaled by what the same counter reads for
@@ -387,6 +438,10 @@ def main():
                     help="turn the fetch/write/copy_fetch/copy_write --pmc csv directories under DIR into "
                          "the attention kernel's traffic record and exit")
     ap.add_argument("--traffic-command", default="", help="command line recorded with --summarize-traffic")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="per-kernel counter summary (MFMA busy, clock, instruction mix, waits, LDS bank "
+                         "conflicts, L2 hits) from the COUNTER_PASSES rocprofv3 directories under DIR and exit")
+    ap.add_argument("--print-counter-pass", metavar="NAME", help="print the counters of one pass and exit")
     ap.add_argument("--modes", action="store_true",
                     help="compare the method, its zeroth-order-only ablation, keep-or-drop and dense attention "
                          "on the workload (markdown table) and exit")
@@ -403,6 +458,12 @@ def main():
         return
     if args.summarize_traffic:
         summarize_traffic(args.summarize_traffic, args.traffic_command)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
+    if args.print_counter_pass:
+        print(COUNTER_PASSES[args.print_counter_pass])
         return
 
     if args.copy_calibration:
