@@ -36,10 +36,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_bf16_wan720p_traffic.json"
 
 
 def source_sha(path: str) -> str:
+    """Hash of the attention kernel's code (its source and dev_common.h) with comments and
+    whitespace removed: a traffic record stays valid across comment edits, not across code edits."""
+    import re
     files = [path, os.path.join(os.path.dirname(path), "dev_common.h")]
     h = hashlib.sha256()
     for f in files:
-        h.update(open(f, "rb").read())
+        text = open(f).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

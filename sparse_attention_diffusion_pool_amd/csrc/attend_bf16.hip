@@ -17,11 +17,13 @@
 // Keys stream in steps of 64 through two LDS stages (K and V halves, 16 KB each): step s + 1 is
 // copied global -> LDS (buffer loads, rows past the block end read as zero) while step s is
 // computed. A key block of 128 rows takes two steps; the selected block list is staged in LDS.
-// Softmax runs in the log2 domain (scale * log2 e folded into one FMA); the accumulators are
-// rescaled only when a row's max grows by more than 2^8 (exact: numerator and denominator share
-// the stale reference, and p <= 256 stays far inside fp32/bf16 range).
+// Softmax runs in the log2 domain: Q is pre-scaled by scale * log2 e, and each score tile starts
+// from one MFMA that adds -m (the row's reference, exact in bf16), so the accumulators hold the
+// exponent arguments. The reference and the accumulators are rescaled only when a row's max grows
+// by more than 2^8 (exact: numerator and denominator share the stale reference, and p <= 256
+// stays far inside fp32/bf16 range).
 // Phase 2: pooled tokens (kbar_j, vbar_j), bias log2 n_j, masked to j in U_i (bit mask in LDS) and
-// j < N_b; beta += p / n_j. Phase 3: O += (beta * scale) (q H-bar).
+// j < N_b; beta += p / n_j. Phase 3: O += (beta * scale) (q H-bar), from the pre-scaled q.
 // Epilogue: out = O / l, rounded to bf16, staged through LDS for 16-byte row stores.
 #include "dev_common.h"
 #include "pisa_internal.h"
