@@ -139,7 +139,11 @@ void derive(pisa::Dims& dm, double keep) {
   if (kk < 1) kk = 1;
   if (kk > dm.Nb) kk = dm.Nb;
   dm.k = (int)kk;
-  dm.NC = (dm.Nb + pisa::kStatsChunk - 1) / pisa::kStatsChunk;
+  // statistics workgroups: chunks of 16 blocks, halved (down to 4) while there are fewer than
+  // 512 workgroups (two per CU), so that small layers still fill the chip
+  dm.chunk = pisa::kStatsChunk;
+  while (dm.chunk > 4 && (long long)((dm.Nb + dm.chunk - 1) / dm.chunk) * dm.H < 512) dm.chunk /= 2;
+  dm.NC = (dm.Nb + dm.chunk - 1) / dm.chunk;
   dm.Nbp = ((dm.Nb + dm.B - 1) / dm.B) * dm.B;
 }
 

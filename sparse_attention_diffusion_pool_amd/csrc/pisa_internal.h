@@ -7,7 +7,8 @@
 
 namespace pisa {
 
-// Blocks whose K^T V products one statistics workgroup sums before writing a partial of H-bar.
+// Most blocks whose K^T V products one statistics workgroup sums before writing a partial of
+// H-bar (Dims::chunk is this, or less for layers too small to fill the chip with 16).
 constexpr int kStatsChunk = 16;
 
 struct Dims {
@@ -18,7 +19,7 @@ struct Dims {
   int Nb;      // ceil(L / B)
   int k;       // critical blocks per query block
   int n_last;  // rows of the last block
-  int NC;      // ceil(Nb / kStatsChunk): partial H-bar sums per head
+  int NC;      // ceil(Nb / chunk): partial H-bar sums per head
   int Nbp;     // Nb rounded up to a multiple of B (pooled-token tiles)
   float scale; // softmax scale applied to q
   int routing; // 0 covariance-aware, 1 plain
@@ -26,6 +27,7 @@ struct Dims {
   int dtype;   // 0 bf16, 1 fp32
   int first_block;  // 1: block-wise first-order term (per-block H_j) instead of H-bar
   int spectral;     // 1: M_j = spectral norm of H_j - H-bar (default Frobenius)
+  int chunk;        // blocks per statistics workgroup (<= kStatsChunk)
 };
 
 // The block-wise first-order variant runs when it is requested and there is a first-order term.

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void stats_pass_bf16(Dims dm, Work w, const __
   const int h = blockIdx.y, c = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int j0 = c * kStatsChunk, j1 = min(dm.Nb, j0 + kStatsChunk);
+  const int j0 = c * dm.chunk, j1 = min(dm.Nb, j0 + dm.chunk);
   const size_t head = (size_t)h * dm.L * 128;
   f32x16 acc[4];
   for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x16{};
@@ -403,8 +403,8 @@ __global__ __launch_bounds__(256) void stats_f32(Dims dm, Work w, const float* _
     j0 = blockIdx.x;
     j1 = j0 + 1;
   } else {
-    j0 = blockIdx.x * kStatsChunk;
-    j1 = min(dm.Nb, j0 + kStatsChunk);
+    j0 = blockIdx.x * dm.chunk;
+    j1 = min(dm.Nb, j0 + dm.chunk);
   }
   float acc[P][P];
   for (int x = 0; x < P; ++x)
