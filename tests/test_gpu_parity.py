@@ -174,6 +174,29 @@ def test_full_size_layers(cfg):
 
 
 # ---------------------------------------------------------------------------------------------
+# Large block counts: the routing kernel's N_b > 1024 variants, and the largest supported layer
+# (N_b = 8192) with k > 4096, where the attention kernel reads the selection list from global
+# memory instead of LDS. Whole selection and statistics of the head; outputs on sampled blocks.
+# ---------------------------------------------------------------------------------------------
+
+LARGE = [
+    # name, grid, keep
+    ("bf16-nb1486-ragged", (29, 83, 79), 0.1),
+    ("bf16-nb8192-k4916", (64, 128, 128), 0.6),
+]
+
+
+@pytest.mark.parametrize("case", LARGE, ids=[c[0] for c in LARGE])
+def test_large_block_counts(case):
+    name, grid, keep = case
+    w = custom(name, 1, grid, 128, 128, keep, "bf16")
+    res = gpu_run(w, want_stats=True)
+    nb = res["info"]["n_blocks"]
+    log(f"[parity] {name}: N_b={nb} k={res['info']['k']}")
+    _full_check(res, heads=[0], label=name, query_blocks=sample_blocks(nb, 4, seed=nb))
+
+
+# ---------------------------------------------------------------------------------------------
 # Determinism and stage equivalence.
 # ---------------------------------------------------------------------------------------------
 
