@@ -44,6 +44,35 @@ __device__ __forceinline__ void ktv_mfma(const char* Ks, const char* Vs, f32x16 
   }
 }
 
+// The same product, plus the block's column sums on the matrix unit: ksum = K^T 1 (the K^T operand
+// against a ones operand) and vsum = 1^T V for the wave's own 32 columns. Products with 1.0 are
+// exact and the sums accumulate in fp32. Rows past the block end are zero in the tiles.
+// Lane l holds: ksum[x] = column sum of K for d = 32 wave + 8 (x >> 2) + 4 (l >> 5) + (x & 3);
+// vsum[0] = column sum of V for column 32 wave + (l & 31).
+template <int BLK>
+__device__ __forceinline__ void ktv_mfma_sums(const char* Ks, const char* Vs, f32x16 acc[4], f32x16& ksum,
+                                              f32x16& vsum, int wave, int lane) {
+  const uint32_t hh = lane >> 5, g16 = (lane >> 4) & 1, l16 = lane & 15;
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+  ksum = f32x16{};
+  vsum = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < BLK / 16; ++ks) {
+    const uint32_t klo = 16 * ks + 8 * hh;
+    const bf16x8 a = tr_operand(Ks, klo, klo + 4, 32 * wave + 16 * g16, l16);
+    ksum = mfma32(a, ones, ksum);
+    const bf16x8 bw = tr_operand(Vs, klo, klo + 4, 32 * wave + 16 * g16, l16);
+    vsum = mfma32(ones, bw, vsum);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const bf16x8 b = tr_operand(Vs, klo, klo + 4, 32 * ct + 16 * g16, l16);
+      acc[ct] = mfma32(a, b, acc[ct]);
+    }
+  }
+}
+
 template <int V>
 struct Stage {
   static constexpr int value = V;
@@ -61,7 +90,7 @@ __global__ __launch_bounds__(256) void stats_pass_bf16(Dims dm, Work w, const __
   __shared__ __attribute__((aligned(1024))) char Vs0[BLK * 256];
   __shared__ __attribute__((aligned(1024))) char Ks1[BLK * 256];
   __shared__ __attribute__((aligned(1024))) char Vs1[BLK * 256];
-  __shared__ float red[4][3][128];
+  __shared__ float red[4][128];  // per-wave column sums of Q
   __shared__ float skb[kStatsChunk][128];  // centroids and value sums of the chunk's blocks
   __shared__ float svs[kStatsChunk][128];
   constexpr int QR = BLK / 16;  // Q rows (16-byte pieces) per thread
@@ -92,48 +121,43 @@ __global__ __launch_bounds__(256) void stats_pass_bf16(Dims dm, Work w, const __
     const char* Ks = ST ? Ks1 : Ks0;
     const char* Vs = ST ? Vs1 : Vs0;
     const int n = rows_of(j);
-    float qs[8] = {0, 0, 0, 0, 0, 0, 0, 0}, ks8[8] = {0, 0, 0, 0, 0, 0, 0, 0}, vs8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const float inv = 1.0f / (float)n;
+    const size_t ob = ((size_t)h * dm.Nb + j) * 128;
+    // Q (in registers): VALU sums over this thread's rows, then across the 16-lane row groups
+    float qs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int e = 0; e < QR; ++e) {
       float f[8];
       unpack_bf16x8(qr[e], f);
       for (int x = 0; x < 8; ++x) qs[x] += f[x];
     }
-    for (int r = rg; r < BLK; r += 16) {
-      float f[8];
-      unpack_bf16x8(*reinterpret_cast<const u32x4*>(Ks + r * 256 + swz_tr(r, p) * 16), f);
-      for (int x = 0; x < 8; ++x) ks8[x] += f[x];
-      unpack_bf16x8(*reinterpret_cast<const u32x4*>(Vs + r * 256 + swz_tr(r, p) * 16), f);
-      for (int x = 0; x < 8; ++x) vs8[x] += f[x];
-    }
     for (int x = 0; x < 8; ++x) {
       qs[x] += __shfl_xor(qs[x], 16);
       qs[x] += __shfl_xor(qs[x], 32);
-      ks8[x] += __shfl_xor(ks8[x], 16);
-      ks8[x] += __shfl_xor(ks8[x], 32);
-      vs8[x] += __shfl_xor(vs8[x], 16);
-      vs8[x] += __shfl_xor(vs8[x], 32);
     }
-    if (lane < 16) {
-      for (int x = 0; x < 8; ++x) {
-        red[wave][0][8 * p + x] = qs[x];
-        red[wave][1][8 * p + x] = ks8[x];
-        red[wave][2][8 * p + x] = vs8[x];
+    if (lane < 16)
+      for (int x = 0; x < 8; ++x) red[wave][8 * p + x] = qs[x];
+    // K and V (in LDS): column sums on the matrix unit beside K^T V
+    f32x16 ksum, vsum;
+    ktv_mfma_sums<BLK>(Ks, Vs, acc, ksum, vsum, wave, lane);
+    const uint32_t hh = lane >> 5;
+    if ((lane & 31) == 0) {
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int dcol = 32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3);
+        w.kbar[ob + dcol] = ksum[x] * inv;
+        skb[j - j0][dcol] = ksum[x] * inv;
       }
     }
-    ktv_mfma<BLK>(Ks, Vs, acc, wave, lane);
+    if (lane < 32) {
+      const int col = 32 * wave + lane;
+      w.vsum[ob + col] = vsum[0];
+      svs[j - j0][col] = vsum[0];
+    }
     __syncthreads();  // red complete
     if (tid < 128) {
-      const float inv = 1.0f / (float)n;
-      const float sq = red[0][0][tid] + red[1][0][tid] + red[2][0][tid] + red[3][0][tid];
-      const float sk = red[0][1][tid] + red[1][1][tid] + red[2][1][tid] + red[3][1][tid];
-      const float sv = red[0][2][tid] + red[1][2][tid] + red[2][2][tid] + red[3][2][tid];
-      const size_t o = ((size_t)h * dm.Nb + j) * 128 + tid;
-      w.qbar[o] = sq * dm.scale * inv;
-      w.kbar[o] = sk * inv;
-      w.vsum[o] = sv;
-      skb[j - j0][tid] = sk * inv;
-      svs[j - j0][tid] = sv;
+      const float sq = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+      w.qbar[ob + tid] = sq * dm.scale * inv;
     }
   };
 
