@@ -152,6 +152,7 @@ hipError_t launch_route(const Dims& dm, const Work& w, hipStream_t s) {
                      dim3(256), 0, s, dm, w)
   if (dm.d == 128) {
     if (ns <= 4) PISA_ROUTE(128, 4, 4);
+    else if (ns <= 12) PISA_ROUTE(128, 12, 4);
     else if (ns <= 16) PISA_ROUTE(128, 16, 4);
     else if (ns <= 32) PISA_ROUTE(128, 32, 2);
     else PISA_ROUTE(128, 128, 1);
