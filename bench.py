@@ -437,6 +437,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="index into workloads.CONFIGS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quality", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the dense-attention comparison (profiled runs: it launches the same kernel)")
     ap.add_argument("--cpu-heads", type=int, default=5)
     ap.add_argument("--phases", type=int, default=7)
     ap.add_argument("--routing", choices=("cov", "plain"), default="cov")
@@ -575,7 +577,7 @@ def main():
                      "frac": round(attend_tflops / peak, 4), "traffic": traffic},
     }
 
-    if w.dtype == "bf16" and args.phases == 7:
+    if w.dtype == "bf16" and args.phases == 7 and not args.no_context:
         # dense attention of the same layer through the same kernel (keep = 1, exact phase only)
         plan_dense = L.Plan(w.L, w.H, w.d, w.B, 1.0, dtype=dtype, phases=1)
         plan_dense.attach_workspace(device=dev)
