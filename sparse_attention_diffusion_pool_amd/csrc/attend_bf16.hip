@@ -193,41 +193,42 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
     atomicOr(&selm[j >> 5], 1u << (j & 31));
   }
   __syncthreads();
-  auto block_of = [&](int t) -> int {  // t-th selected block (wave-uniform)
-    return __builtin_amdgcn_readfirstlane(kk <= kIdxLds ? (int)sidx[t] : sel[t]);
+  auto block_raw = [&](int t) -> int {  // t-th selected block (uniform, held per lane)
+    return kk <= kIdxLds ? (int)sidx[t] : sel[t];
   };
 
   // Steps: exact (two per 128-row block; the ragged last block, which is last if selected, drops
   // its second half when n_last <= 64), then pooled tiles, then the H-bar^T tile (128 rows over
   // both arrays of a stage).
-  const int last_blk = block_of(kk - 1);
+  const int last_blk = __builtin_amdgcn_readfirstlane(block_raw(kk - 1));
   const int rows_last = last_blk == Nb - 1 ? dm.n_last : B;
   const int E = (kk - 1) * SPB + (rows_last + kKT - 1) / kKT;  // exact steps
   const bool ragged = (rows_last % kKT) != 0;                   // last exact step is partial
   const int S_main = E + nc * SPB;
   const int S_all = S_main + (do_first ? 1 : 0);
 
-  const uint32_t vb_row = copy_vbase<false>(wave, lane), vb_tr = copy_vbase<true>(wave, lane);
-  const uint32_t vb_row2 = copy_vbase<false>(wave, lane, 8), vb_tr2 = copy_vbase<true>(wave, lane, 8);
+  // Byte offsets inside Q, K and V fit in 32 bits (the plan keeps H L d below 2^31 elements).
+  const char* Kh = reinterpret_cast<const char*>(K + head);
+  const char* Vh = reinterpret_cast<const char*>(V + head);
+  const uint32_t cl_row = chunk_lane<false>(lane), cl_tr = chunk_lane<true>(lane);
   auto issue = [&](int s, auto stc) {
     constexpr int ST = decltype(stc)::value;
-    char* Ks = ST ? sK1 : sK0;
-    char* Vs = ST ? sV1 : sV0;
+    const uint32_t Ks = lds_addr(ST ? sK1 : sK0), Vs = lds_addr(ST ? sV1 : sV0);
     if (s < E) {
-      const int j = block_of(s / SPB);
+      const int j = __builtin_amdgcn_readfirstlane(block_raw(s / SPB));
       const int r0 = kKT * (s % SPB);
       const int n_j = (j == Nb - 1) ? dm.n_last : B;
-      const size_t g0 = head + ((size_t)j * B + r0) * 128;
+      const uint32_t off = ((uint32_t)j * (uint32_t)B + (uint32_t)r0) * 256u;
       const uint32_t bytes = (uint32_t)(n_j - r0) * 256;  // rows past the block end read as zero
-      copy_tile_async<kKT, NW>(rsrc_words(K + g0, bytes), lds_addr(Ks), vb_row, wave, vb_row2);
-      copy_tile_async<kKT, NW>(rsrc_words(V + g0, bytes), lds_addr(Vs), vb_tr, wave, vb_tr2);
+      copy_tile_chunks<kKT, NW, false>(rsrc_words(Kh + off, bytes), Ks, cl_row, wave);
+      copy_tile_chunks<kKT, NW, true>(rsrc_words(Vh + off, bytes), Vs, cl_tr, wave);
     } else if (s < S_main) {
       const size_t g0 = (size_t)(s - E) * kKT * 128;
-      copy_tile_async<kKT, NW>(rsrc_words(kl + g0, kKT * 256), lds_addr(Ks), vb_row, wave, vb_row2);
-      copy_tile_async<kKT, NW>(rsrc_words(vl + g0, kKT * 256), lds_addr(Vs), vb_tr, wave, vb_tr2);
+      copy_tile_chunks<kKT, NW, false>(rsrc_words(kl + g0, kKT * 256), Ks, cl_row, wave);
+      copy_tile_chunks<kKT, NW, true>(rsrc_words(vl + g0, kKT * 256), Vs, cl_tr, wave);
     } else {
-      copy_tile_async<kKT, NW>(rsrc_words(ht, kKT * 256), lds_addr(Ks), vb_row, wave, vb_row2);
-      copy_tile_async<kKT, NW>(rsrc_words(ht + kKT * 128, kKT * 256), lds_addr(Vs), vb_row, wave, vb_row2);
+      copy_tile_chunks<kKT, NW, false>(rsrc_words(ht, kKT * 256), Ks, cl_row, wave);
+      copy_tile_chunks<kKT, NW, false>(rsrc_words(ht + kKT * 128, kKT * 256), Vs, cl_row, wave);
     }
   };
   issue(0, Stage<0>{});
@@ -258,6 +259,10 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) O[dt] = f32x16{};
   const LaneOffsets lofs = lane_offsets(lane);
+  // The two waves sharing a SIMD come from different workgroups. A fixed priority order between
+  // them (by the parity of the hardware wave slot, HW_ID bits 0..3) lets one run at its own pace
+  // while the other fills its gaps, instead of both competing for every issue slot.
+  if (__builtin_amdgcn_s_getreg((4 << 0) | (0 << 6) | (3 << 11)) & 1) __builtin_amdgcn_s_setprio(2);
 
   // One step s (ST = s & 1). KIND 0 = exact, 1 = exact partial (masked past valid rows), 2 = pooled.
   auto step = [&](int s, auto stc, auto kc) {

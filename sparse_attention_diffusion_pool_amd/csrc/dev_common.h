@@ -49,25 +49,6 @@ __device__ __forceinline__ void wait_vmem() {
   __asm__ __volatile__("" ::: "memory");
 }
 
-// The same direct copy (16 bytes per lane, lane l's bytes at lds_base + soff_lds + 16 l, global
-// offset voff + soff), issued from inline assembly. The compiler's wait-count insertion cannot tell
-// direct-to-LDS copies into one buffer from reads of another, so after a copy issued through the
-// builtin it makes every later LDS read wait for the copy; from assembly it does not see the copy
-// at all, and the caller waits for completion itself (wait_vmem) before reading the destination.
-// The instruction has no register results; its address operands are read when it issues.
-// lds_base is an LDS byte address (lds_addr of a __shared__ object plus an offset).
-__device__ __forceinline__ void buf_load_lds16_async(const u32x4& rsrc, uint32_t lds_base, uint32_t voff, uint32_t soff) {
-  // the LDS base, the resource and the scalar offset are wave-uniform: pin them to SGPRs
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_base);
-  const u32x4 r = {(uint32_t)__builtin_amdgcn_readfirstlane(rsrc[0]), (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[1]),
-                   (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[2]), (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[3])};
-  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(m0v), "v"(voff), "s"(r), "s"(so)
-               : "memory", "m0");
-}
-
 // LDS byte address of a __shared__ object. Applied to the object itself it folds to a constant;
 // kept as a 32-bit address afterwards, the copies need no generic-to-LDS pointer conversion
 // (with its null check) per instruction.
@@ -75,7 +56,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// Buffer resource words for buf_load_lds16_async (same format as make_rsrc).
+// Buffer resource words for copy_chunk_async (same format as make_rsrc).
 __device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
   const uint64_t a = (uint64_t)(uintptr_t)base;
   return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, kRsrcWord3};
@@ -147,15 +128,74 @@ __device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t r, char* lds, u
                                              (NWAVES == 2 ? (m & ~1) : m) * NWAVES * 1024, 0, 0);
 }
 
-// copy_tile through buf_load_lds16_async (rsrc from rsrc_words).
-template <int ROWS, int NWAVES>
-__device__ __forceinline__ void copy_tile_async(const u32x4& r, uint32_t lds, uint32_t vbase, int wave,
-                                                uint32_t vbase2 = 0) {
-  static_assert((NWAVES % 4 == 0 || NWAVES == 2) && ROWS % (4 * NWAVES) == 0, "copy_tile layout");
+// Per-lane global offset of a 16-row chunk copy. Instruction m (0..3) of a chunk covers chunk rows
+// 4 m .. 4 m + 3: lane l reads row 4 m + l / 16 at the swizzle's source chunk for stored chunk l % 16.
+// The row's 1024 m bytes are not included: the instruction offset adds them, and on a direct-to-LDS
+// load it moves the LDS destination by the same amount (both checked on gfx950 with an in-bounds
+// probe, as is that the buffer range check covers the scalar and instruction offsets).
+// What remains depends on m only through the swizzle. Transpose-read tiles swizzle by row & 3 =
+// l / 16, the same for every m. Row-read tiles swizzle by row & 15 = 4 m | l / 16, and XOR-ing the
+// chunk with 4 m flips bits 6..7 of the byte offset: instruction m's offset is m = 0's XOR 64 m.
+template <bool TR>
+__device__ __forceinline__ uint32_t chunk_lane(int lane) {
+  const uint32_t row = lane >> 4, pos = lane & 15;
+  const uint32_t chunk = TR ? swz_tr(row, pos) : swz_row(row, pos);
+  return row * 256 + chunk * 16;
+}
+
+// Direct copy of one 16-row chunk (4 KB) global -> LDS from inline assembly: one m0 write, four
+// loads. lds = the chunk's LDS byte address, soff = its global byte offset within the resource,
+// v0 = chunk_lane<TR>(lane). Bytes past the resource's range are written as 0.
+// Issued from assembly because the compiler's wait-count insertion cannot tell direct-to-LDS copies
+// into one buffer from reads of another: after a copy through the builtin it makes every later LDS
+// read wait for the copy. From assembly it does not see the copy at all, so the caller waits for
+// completion itself (wait_vmem) before reading the destination. The instructions have no register
+// results; their address operands are read when they issue. The row layout's other three offsets
+// are formed inside the block in scratch registers (kept out of the loop, they would hold three
+// registers for the whole kernel).
+template <bool TR>
+__device__ __forceinline__ void copy_chunk_async(const u32x4& rsrc, uint32_t lds, uint32_t v0, uint32_t soff) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+  const u32x4 r = {(uint32_t)__builtin_amdgcn_readfirstlane(rsrc[0]), (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[1]),
+                   (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[2]), (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[3])};
+  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+  if constexpr (TR) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen offset:1024 lds\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen offset:2048 lds\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen offset:3072 lds"
+        :
+        : "s"(m0v), "v"(v0), "s"(r), "s"(so)
+        : "memory", "m0");
+  } else {
+    uint32_t t1, t2, t3;
+    asm volatile(
+        "s_mov_b32 m0, %3\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %4, %5, %6 offen lds\n\t"
+        "v_xor_b32 %0, 64, %4\n\t"
+        "v_xor_b32 %1, 0x80, %4\n\t"
+        "v_xor_b32 %2, 0xc0, %4\n\t"
+        "buffer_load_dwordx4 %0, %5, %6 offen offset:1024 lds\n\t"
+        "buffer_load_dwordx4 %1, %5, %6 offen offset:2048 lds\n\t"
+        "buffer_load_dwordx4 %2, %5, %6 offen offset:3072 lds"
+        : "=&v"(t1), "=&v"(t2), "=&v"(t3)
+        : "s"(m0v), "v"(v0), "s"(r), "s"(so)
+        : "memory", "m0");
+  }
+}
+
+// Direct copy of a ROWS x 256 B tile (rsrc from rsrc_words) by NWAVES waves in 16-row chunks: wave w
+// copies chunks w, w + NWAVES, ...; v0 = chunk_lane<TR>(lane).
+template <int ROWS, int NWAVES, bool TR>
+__device__ __forceinline__ void copy_tile_chunks(const u32x4& r, uint32_t lds, uint32_t v0, int wave) {
+  static_assert(ROWS % (16 * NWAVES) == 0, "tile rows must split into 16-row chunks over the waves");
 #pragma unroll
-  for (int m = 0; m < ROWS / 4 / NWAVES; ++m)
-    buf_load_lds16_async(r, lds + 1024u * (m * NWAVES + wave), (NWAVES == 2 && (m & 1)) ? vbase2 : vbase,
-                         (NWAVES == 2 ? (m & ~1) : m) * NWAVES * 1024);
+  for (int n = 0; n < ROWS / 16 / NWAVES; ++n) {
+    const uint32_t c = n * NWAVES + wave;
+    copy_chunk_async<TR>(r, lds + 4096u * c, v0, 4096u * c);
+  }
 }
 
 // extra_rows: 0, or 8 for the odd instructions of a 2-wave copy
