@@ -22,8 +22,11 @@
 // exponent arguments. The reference and the accumulators are rescaled only when a row's max grows
 // by more than 2^8 (exact: numerator and denominator share the stale reference, and p <= 256
 // stays far inside fp32/bf16 range).
-// Phase 2: pooled tokens (kbar_j, vbar_j), bias log2 n_j, masked to j in U_i (bit mask in LDS) and
-// j < N_b; beta += p / n_j. Phase 3: O += (beta * scale) (q H-bar), from the pre-scaled q.
+// Phase 2: pooled tokens (kbar_j, vbar_j) through the same steps; each token's bias (log2 n_j, or
+// -inf outside U_i, from the bit mask in LDS, or past N_b) enters through the shift MFMA, so the
+// softmax is the exact steps' own. beta (the sum of p / n_j) takes each pooled step's row sum over
+// B, plus a correction for a ragged last block's token. Phase 3: O += (beta * scale) (q H-bar),
+// from the pre-scaled q.
 // Epilogue: out = O / l, rounded to bf16, staged through LDS for 16-byte row stores.
 #include "dev_common.h"
 #include "pisa_internal.h"
@@ -248,12 +251,26 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
   for (int s = 0; s < 8; ++s)
 #pragma unroll
     for (int e = 0; e < 8; ++e) qreg[s][e] = (__bf16)((float)qreg[s][e] * cs);
-  // A operand of the shift MFMA: A[key][k] = (k == 0), so A x B adds row 0 of B to every key.
-  // B: row 0 holds -m of the lane's query (0 while m = -inf); it changes only with m.
+  // Operands of the shift MFMA that starts every score tile, D[key][q] = sum over k < 3 of
+  // A[key][k] B[k][q]: B row 0 holds -m of the lane's query (0 while m = -inf; it changes only with
+  // m), rows 1 and 2 hold 1. A column 0 is 1; columns 1 and 2 are the key's bias: 0 for exact keys;
+  // for a pooled token log2 n_j, or -inf for a selected block or j >= N_b. log2 B is exact in bf16;
+  // the ragged last block's log2 n_last is split into a bf16 head (column 1) and tail (column 2).
   bf16x8 shift_a = {}, shift_b = {};
   shift_a[0] = (__bf16)(hh == 0 ? 1.0f : 0.0f);
+  shift_b[1] = (__bf16)(hh == 0 ? 1.0f : 0.0f);
+  shift_b[2] = shift_b[1];
   const float lgB = __log2f((float)B), lgLast = __log2f((float)dm.n_last);
-  const float invB = 1.0f / (float)B, invLast = 1.0f / (float)dm.n_last;
+  const __bf16 lgLast_hi = (__bf16)lgLast, lgLast_lo = (__bf16)(lgLast - (float)lgLast_hi);
+  const float invB = 1.0f / (float)B;
+  // beta takes a pooled step's row sum over B. For a ragged last block (n_last < B) the step that
+  // holds its token (s_last) adds p (1 / n_last - 1 / B), with p read from the token's accumulator:
+  // key row i = (N_b - 1) % 32 of subtile u_last, in lanes with hh = (i / 4) % 2, element
+  // (i % 4) + 4 (i / 8).
+  const int s_last = dm.n_last != B ? E + (Nb - 1) / kKT : -1;
+  const int r_last = (Nb - 1) % kKT, i_last = r_last % 32;
+  const int u_last = r_last / 32, hh_last = (i_last / 4) % 2, x_last = (i_last % 4) + 4 * (i_last / 8);
+  const float corr_last = 1.0f / (float)dm.n_last - invB;
   float m = -INFINITY, lsum = 0.f, beta = 0.f;
   f32x16 O[4];
 #pragma unroll
@@ -276,46 +293,39 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
     // The accumulators start at -m (m is exact in bf16), so the MFMA returns the exponent argument
     // cs q.k - m and the softmax needs no FMA per score. (A lane whose keys have all been masked so
     // far still has m = -inf: its shift is 0.)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) Sc[t] = mfma32(shift_a, shift_b, f32x16{});
-    qk_tile<NT, true>(ST ? sK1 : sK0, 0, qreg, Sc, lofs);
-    float mx = -INFINITY;  // of the scores relative to mref
-    // pooled token of this lane's element c = 0 (element x adds 32 u + 8 (x >> 2) + (x & 3)); made
-    // opaque per step so that the per-element constants are not hoisted out of the step loop,
-    // where they would pin about 32 registers and force spills
-    int jb = (s - E) * kKT + 4 * (int)hh;
-    if constexpr (KIND == 2) asm volatile("" : "+v"(jb));
     if constexpr (KIND == 2) {
-      const int key_base = (s - E) * kKT;  // pooled token index of the step's first key
+      // A row = key l32 of subtile t: pooled token j = (s - E) kKT + 32 t + l32
+      const int key_base = (s - E) * kKT;
 #pragma unroll
-      for (int u = 0; u < NT; ++u) {
-        const uint32_t word = selm[(key_base + 32 * u) / 32] >> (4 * hh);
-#pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const int c = 8 * (x >> 2) + (x & 3);
-          const int j = jb + 32 * u + c;
-          const bool ok = j < Nb && !((word >> c) & 1u);
-          const float lg = ok ? (j == Nb - 1 ? lgLast : lgB) : -INFINITY;
-          Sc[u][x] += lg;
-          mx = fmaxf(mx, Sc[u][x]);
-        }
+      for (int t = 0; t < NT; ++t) {
+        const int j = key_base + 32 * t + (int)l32;
+        const bool sel_j = (selm[(key_base + 32 * t) / 32] >> l32) & 1u;
+        const bool ok = j < Nb && !sel_j && hh == 0;
+        bf16x8 a = shift_a;
+        a[1] = ok ? (j == Nb - 1 ? lgLast_hi : (__bf16)lgB) : (__bf16)(hh == 0 ? -INFINITY : 0.0f);
+        a[2] = ok && j == Nb - 1 ? lgLast_lo : (__bf16)0.0f;
+        Sc[t] = mfma32(a, shift_b, f32x16{});
       }
     } else {
-      if constexpr (KIND == 1) {
-        const int valid = rows_last - kKT * ((E - 1) % SPB);  // rows of the partial step
 #pragma unroll
-        for (int u = 0; u < NT; ++u)
-#pragma unroll
-          for (int x = 0; x < 16; ++x) {
-            const int key = 32 * u + 8 * (x >> 2) + 4 * hh + (x & 3);
-            if (key >= valid) Sc[u][x] = -INFINITY;
-          }
-      }
+      for (int t = 0; t < NT; ++t) Sc[t] = mfma32(shift_a, shift_b, f32x16{});
+    }
+    qk_tile<NT, true>(ST ? sK1 : sK0, 0, qreg, Sc, lofs);
+    float mx = -INFINITY;  // of the scores relative to mref
+    if constexpr (KIND == 1) {
+      const int valid = rows_last - kKT * ((E - 1) % SPB);  // rows of the partial step
 #pragma unroll
       for (int u = 0; u < NT; ++u)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) mx = fmaxf(mx, Sc[u][x]);
+        for (int x = 0; x < 16; ++x) {
+          const int key = 32 * u + 8 * (x >> 2) + 4 * hh + (x & 3);
+          if (key >= valid) Sc[u][x] = -INFINITY;
+        }
     }
+#pragma unroll
+    for (int u = 0; u < NT; ++u)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) mx = fmaxf(mx, Sc[u][x]);
     mx = xor32_max(mx);
     const bool up = mx > (m == -INFINITY ? -INFINITY : kLazy);
     if (__builtin_expect(__ballot(up) != 0, 0)) {
@@ -332,34 +342,42 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
 #pragma unroll
       for (int u = 0; u < NT; ++u) Sc[u] -= shift;
     }
+    // score of the ragged last block's token in its step (wave-uniform branch), taken before the
+    // exponentials so that the score registers need not outlive them
+    float s_tok = -INFINITY;
+    if constexpr (KIND == 2) {
+      if (s == s_last) {
+        s_tok = Sc[0][x_last];
+#pragma unroll
+        for (int u = 1; u < NT; ++u)
+          if (u == u_last) s_tok = Sc[u][x_last];
+      }
+    }
 #pragma unroll
     for (int u = 0; u < NT; ++u)
 #pragma unroll
       for (int v = 0; v < 2; ++v)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int x = 8 * v + e;
-          float p;
-          if constexpr (KIND == 2) {
-            const int j = jb + 32 * u + 8 * (x >> 2) + (x & 3);
-            p = __builtin_amdgcn_exp2f(Sc[u][x]);
-            beta = fmaf(p, j == Nb - 1 ? invLast : invB, beta);
-          } else {
-            p = __builtin_amdgcn_exp2f(Sc[u][x]);
-          }
-          if constexpr (KIND == 2) lsum += p;
-          P[u][v][e] = (__bf16)p;
-        }
-    if constexpr (KIND != 2) {
-      // row sum of the rounded probabilities (those the numerator's MFMA uses), two per dot2
+        for (int e = 0; e < 8; ++e) P[u][v][e] = (__bf16)__builtin_amdgcn_exp2f(Sc[u][8 * v + e]);
+    {
+      // row sum of the rounded probabilities (those the numerator's MFMA uses), two per dot2;
+      // a pooled step's sum, divided by the block size, also feeds beta
       const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      float ps = KIND == 2 ? 0.0f : lsum;
 #pragma unroll
       for (int u = 0; u < NT; ++u)
 #pragma unroll
         for (int v = 0; v < 2; ++v)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P[u][v][2 * e], P[u][v][2 * e + 1]}, ones, lsum, false);
+            ps = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P[u][v][2 * e], P[u][v][2 * e + 1]}, ones, ps, false);
+      if constexpr (KIND == 2) {
+        lsum += ps;
+        beta = fmaf(ps, invB, beta);
+        if (s == s_last && (int)hh == hh_last) beta = fmaf(__builtin_amdgcn_exp2f(s_tok), corr_last, beta);
+      } else {
+        lsum = ps;
+      }
     }
     pv_tile<NT>(ST ? sV1 : sV0, 0, P, O, lofs);
   };
