@@ -73,54 +73,44 @@ __device__ __forceinline__ void ktv_mfma_sums(const char* Ks, const char* Vs, f3
   }
 }
 
-template <int V>
-struct Stage {
-  static constexpr int value = V;
-};
-
-// Pass A, bf16. The K and V tiles of block j + 1 are copied to LDS (and its Q rows loaded into
-// registers) while block j is summed and multiplied, through two LDS stages held as distinct
-// objects. The chunk's partial is written already corrected by the centroids:
-// G_c = sum_{j in c} (K_j^T V_j - kbar_j (sum V_j)^T) = sum_{j in c} H_j.
+// Pass A, bf16. One LDS stage (64 KB) and two workgroups per CU: each workgroup copies a block's K
+// and V tiles to LDS (Q rows into registers), then sums and multiplies them, while the other
+// workgroup on the CU has its block in flight. (Two stages in one workgroup would keep only one
+// block in flight per CU: LDS holds about two blocks.) The chunk's partial is corrected by the
+// centroids block by block: G_c = sum_{j in c} (K_j^T V_j - kbar_j (sum V_j)^T) = sum_{j in c} H_j.
 template <int BLK>
-__global__ __launch_bounds__(256) void stats_pass_bf16(Dims dm, Work w, const __bf16* __restrict__ Q,
-                                                       const __bf16* __restrict__ K,
-                                                       const __bf16* __restrict__ V) {
-  __shared__ __attribute__((aligned(1024))) char Ks0[BLK * 256];
-  __shared__ __attribute__((aligned(1024))) char Vs0[BLK * 256];
-  __shared__ __attribute__((aligned(1024))) char Ks1[BLK * 256];
-  __shared__ __attribute__((aligned(1024))) char Vs1[BLK * 256];
+__global__ __launch_bounds__(256, 2) void stats_pass_bf16(Dims dm, Work w, const __bf16* __restrict__ Q,
+                                                          const __bf16* __restrict__ K,
+                                                          const __bf16* __restrict__ V) {
+  __shared__ __attribute__((aligned(1024))) char Ks[BLK * 256];
+  __shared__ __attribute__((aligned(1024))) char Vs[BLK * 256];
   __shared__ float red[4][128];  // per-wave column sums of Q
-  __shared__ float skb[kStatsChunk][128];  // centroids and value sums of the chunk's blocks
-  __shared__ float svs[kStatsChunk][128];
-  constexpr int QR = BLK / 16;  // Q rows (16-byte pieces) per thread
+  __shared__ float svs[128];     // the current block's value sums
+  constexpr int QR = BLK / 16;   // Q rows (16-byte pieces) per thread
   const int h = blockIdx.y, c = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j0 = c * dm.chunk, j1 = min(dm.Nb, j0 + dm.chunk);
   const size_t head = (size_t)h * dm.L * 128;
+  const uint32_t hh = lane >> 5, l32 = lane & 31;
   f32x16 acc[4];
   for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x16{};
   const int p = tid & 15, rg = tid >> 4;  // column chunk (8 columns) and row group for the sums
-  u32x4 qa[QR], qb[QR];
+  u32x4 qa[QR];
 
   auto rows_of = [&](int j) { return (j == dm.Nb - 1) ? dm.n_last : dm.B; };
-  auto issue = [&](int j, auto stc, u32x4* qr) {
-    constexpr int ST = decltype(stc)::value;
+  for (int j = j0; j < j1; ++j) {
     const int n = rows_of(j);
     const size_t r0 = head + (size_t)j * dm.B * 128;
-    tile_to_lds<true>(make_rsrc(K + r0, n * 256), 256, ST ? Ks1 : Ks0, BLK, wave, 4, lane);
-    tile_to_lds<true>(make_rsrc(V + r0, n * 256), 256, ST ? Vs1 : Vs0, BLK, wave, 4, lane);
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + r0, n * 256);
+    tile_to_lds<true>(make_rsrc(K + r0, n * 256), 256, Ks, BLK, wave, 4, lane);
+    tile_to_lds<true>(make_rsrc(V + r0, n * 256), 256, Vs, BLK, wave, 4, lane);
+    {
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + r0, n * 256);
 #pragma unroll
-    for (int e = 0; e < QR; ++e) qr[e] = buf_load16(rq, (rg + 16 * e) * 256 + p * 16);
-  };
-
-  auto block = [&](int j, auto stc, const u32x4* qr) {
-    constexpr int ST = decltype(stc)::value;
-    const char* Ks = ST ? Ks1 : Ks0;
-    const char* Vs = ST ? Vs1 : Vs0;
-    const int n = rows_of(j);
+      for (int e = 0; e < QR; ++e) qa[e] = buf_load16(rq, (rg + 16 * e) * 256 + p * 16);
+    }
+    wait_vmem();
+    __syncthreads();  // the block's tiles landed
     const float inv = 1.0f / (float)n;
     const size_t ob = ((size_t)h * dm.Nb + j) * 128;
     // Q (in registers): VALU sums over this thread's rows, then across the 16-lane row groups
@@ -128,7 +118,7 @@ __global__ __launch_bounds__(256) void stats_pass_bf16(Dims dm, Work w, const __
 #pragma unroll
     for (int e = 0; e < QR; ++e) {
       float f[8];
-      unpack_bf16x8(qr[e], f);
+      unpack_bf16x8(qa[e], f);
       for (int x = 0; x < 8; ++x) qs[x] += f[x];
     }
     for (int x = 0; x < 8; ++x) {
@@ -140,52 +130,34 @@ __global__ __launch_bounds__(256) void stats_pass_bf16(Dims dm, Work w, const __
     // K and V (in LDS): column sums on the matrix unit beside K^T V
     f32x16 ksum, vsum;
     ktv_mfma_sums<BLK>(Ks, Vs, acc, ksum, vsum, wave, lane);
-    const uint32_t hh = lane >> 5;
-    if ((lane & 31) == 0) {
+    // lane l's ksum[x] is the column sum of K for row a = 32 wave + 8 (x >> 2) + 4 hh + (x & 3) of
+    // the product, the same row as acc[.][x]
+    if (l32 == 0) {
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int dcol = 32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3);
-        w.kbar[ob + dcol] = ksum[x] * inv;
-        skb[j - j0][dcol] = ksum[x] * inv;
-      }
+      for (int x = 0; x < 16; ++x) w.kbar[ob + 32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3)] = ksum[x] * inv;
     }
     if (lane < 32) {
-      const int col = 32 * wave + lane;
-      w.vsum[ob + col] = vsum[0];
-      svs[j - j0][col] = vsum[0];
+      w.vsum[ob + 32 * wave + lane] = vsum[0];
+      svs[32 * wave + lane] = vsum[0];
     }
-    __syncthreads();  // red complete
+    __syncthreads();  // red and svs complete; every wave done with the tiles
     if (tid < 128) {
       const float sq = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
       w.qbar[ob + tid] = sq * dm.scale * inv;
     }
-  };
-
-  issue(j0, Stage<0>{}, qa);
-  for (int j = j0; j < j1; j += 2) {
-    wait_vmem();
-    __syncthreads();  // stage 0 landed; stage 1 and red free
-    if (j + 1 < j1) issue(j + 1, Stage<1>{}, qb);
-    block(j, Stage<0>{}, qa);
-    if (j + 1 < j1) {
-      wait_vmem();
-      __syncthreads();
-      if (j + 2 < j1) issue(j + 2, Stage<0>{}, qa);
-      block(j + 1, Stage<1>{}, qb);
-    }
-  }
-  __syncthreads();  // skb / svs complete
-  // G[h][c][a][b] = acc - sum_j kbar_j[a] vsum_j[b]
-  float* G = w.G + ((size_t)h * dm.NC + c) * 128 * 128;
-  const int hh = lane >> 5, l32 = lane & 31;
-  for (int jj = 0; jj < j1 - j0; ++jj) {
+    // acc[ct][x] -= kbar_j[a] vsum_j[b], b = 32 ct + l32
     float vb[4];
-    for (int ct = 0; ct < 4; ++ct) vb[ct] = svs[jj][32 * ct + l32];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) vb[ct] = svs[32 * ct + l32];
+#pragma unroll
     for (int x = 0; x < 16; ++x) {
-      const float ka = skb[jj][32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3)];
+      const float ka = ksum[x] * inv;
+#pragma unroll
       for (int ct = 0; ct < 4; ++ct) acc[ct][x] = fmaf(-ka, vb[ct], acc[ct][x]);
     }
+    __syncthreads();  // red and svs read before the next block overwrites them
   }
+  float* G = w.G + ((size_t)h * dm.NC + c) * 128 * 128;
   for (int ct = 0; ct < 4; ++ct)
     for (int x = 0; x < 16; ++x) {
       const int a = 32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3);
