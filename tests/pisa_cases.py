@@ -29,7 +29,7 @@ def log(msg: str) -> None:
 
 
 def gpu_run(w, heads=None, keep=None, B=None, routing=0, phases=7, inputs=None, want_stats=False,
-            stages=False, first_order=0, norm=0):
+            stages=False, first_order=0, norm=0, scale=None):
     q, k, v = inputs if inputs is not None else layer_inputs(w, heads)
     H, Lq, d = q.shape
     B = w.B if B is None else B
@@ -38,12 +38,12 @@ def gpu_run(w, heads=None, keep=None, B=None, routing=0, phases=7, inputs=None, 
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
     dtype = L.DTYPE_BF16 if q.dtype == torch.bfloat16 else L.DTYPE_F32
     plan = L.Plan(Lq, H, d, B, keep, dtype=dtype, routing=routing, phases=phases, first_order=first_order,
-                  norm=norm)
+                  norm=norm, scale=scale)
     plan.attach_workspace(device=dev)
     info = plan.info()
     out = torch.full_like(qd, float("nan"))
     log(f"[gpu] {w.name} H={H} L={Lq} d={d} B={B} keep={keep} k={info['k']} routing={routing} "
-        f"phases={phases} stages={stages} first_order={first_order} norm={norm}")
+        f"phases={phases} stages={stages} first_order={first_order} norm={norm} scale={scale}")
     if stages:
         plan.forward_stats(qd, kd, vd)
         plan.forward_route()
@@ -64,7 +64,7 @@ def gpu_run(w, heads=None, keep=None, B=None, routing=0, phases=7, inputs=None, 
     log(f"[gpu] done {w.name}")
     res = {"out": out.cpu(), "idx": idx.cpu().numpy(), "info": info, "inputs": (q, k, v), "B": B,
            "keep": keep, "routing": routing, "phases": phases, "dtype": w.dtype, "first_order": first_order,
-           "norm": norm}
+           "norm": norm, "scale": scale}
     if stats is not None:
         res["stats"] = {n: t.cpu().numpy().astype(np.float64) for n, t in stats.items()}
     plan.destroy()
@@ -101,11 +101,13 @@ def oracle_head(res, h: int, query_blocks=None):
     if res.get("first_order") == 1 and res["phases"] == 7:
         mode["first_order"] = "block"
     mode["norm"] = "spectral" if res.get("norm") == 1 else "fro"
-    ref = po.pisa_head(q, k, v, B, keep, routing=routing, query_blocks=[], **mode)
+    scale = res.get("scale")
+    ref = po.pisa_head(q, k, v, B, keep, scale=scale, routing=routing, query_blocks=[], **mode)
     nsel = check_selection(res["idx"][h], ref["scores"], ref["S"], ref["k"])
     qb = range(len(ref["S"])) if query_blocks is None else query_blocks
     gsel = [list(map(int, s)) for s in res["idx"][h]]
-    out_ref = po.pisa_head(q, k, v, B, keep, routing=routing, selection=gsel, query_blocks=qb, **mode)["out"]
+    out_ref = po.pisa_head(q, k, v, B, keep, scale=scale, routing=routing, selection=gsel, query_blocks=qb,
+                           **mode)["out"]
     return ref, out_ref, nsel
 
 

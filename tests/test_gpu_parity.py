@@ -86,6 +86,18 @@ def test_small_bf16_modes(phases, routing, B):
     _full_check(res, label=f"bf16 modes B={B} routing={routing} phases={phases}")
 
 
+@pytest.mark.parametrize("scale", [0.05, 0.2])
+@pytest.mark.parametrize("case", [("bf16", 128, 128), ("bf16", 128, 64), ("f32", 64, 128)],
+                         ids=["bf16-B128", "bf16-B64", "f32-d64"])
+def test_small_custom_scale(case, scale):
+    # a softmax scale other than 1/sqrt(d) (PISA_OPT_SCALE): it enters the Q pre-scale, the pooled
+    # queries and scores, and the first-order term
+    dtype, d, B = case
+    w = custom(f"{dtype}-scale", 2, (7, 11, 13), d, B, 0.3, dtype)
+    res = gpu_run(w, scale=scale, want_stats=True)
+    _full_check(res, label=f"{dtype} d={d} B={B} scale={scale}")
+
+
 # ---------------------------------------------------------------------------------------------
 # Block-wise first-order variant (per-block H_j instead of H-bar), against the oracle's
 # first_order="block" mode; with the first-order phase off the option changes nothing.
