@@ -222,6 +222,32 @@ def test_deterministic_and_stages_match_forward():
     assert torch.equal(a["out"], c["out"]) and np.array_equal(a["idx"], c["idx"])
 
 
+def test_two_plans_on_side_streams():
+    # two plans (own workspaces) run concurrently on two non-default streams; each gives the same
+    # bits as a plan on the current stream
+    from sparse_attention_diffusion_pool_amd import _lib as L
+    w = custom("bf16-streams", 2, (7, 11, 13), 128, 128, 0.3, "bf16")
+    dev = torch.device("cuda", 0)
+    qd, kd, vd = (t.to(dev) for t in layer_inputs(w))
+    H, Lq, d = qd.shape
+    plans = [L.Plan(Lq, H, d, w.B, w.keep, dtype=L.DTYPE_BF16) for _ in range(3)]
+    for p in plans:
+        p.attach_workspace(device=dev)
+    outs = [torch.full_like(qd, float("nan")) for _ in range(3)]
+    plans[0].forward(qd, kd, vd, outs[0])
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for s, p, o in zip(streams, plans[1:], outs[1:]):
+        with torch.cuda.stream(s):
+            p.forward(qd, kd, vd, o, stream=s)
+    torch.cuda.synchronize()
+    for p in plans:
+        p.destroy()
+    assert torch.isfinite(outs[0].float()).all()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
 def test_outputs_untouched_outside_rows_and_no_nan():
     # out is pre-filled with NaN by gpu_run: every row must be written, none left NaN
     w = custom("fill", 2, (7, 11, 13), 128, 128, 0.3, "bf16")
