@@ -119,7 +119,9 @@ pisa_status pisa_plan_info(const pisa_plan_t *plan, pisa_plan_info_t *info);
 pisa_status pisa_plan_attach_workspace(pisa_plan_t *plan, void *dev_ptr, size_t bytes);
 
 /* The whole forward pass: statistics, routing, fused piecewise attention. Enqueued on `stream`
- * (asynchronous). Equivalent to pisa_forward_stats + pisa_forward_route + pisa_forward_attend. */
+ * (asynchronous). Equivalent to pisa_forward_stats + pisa_forward_route + pisa_forward_attend.
+ * It only launches kernels (no allocation, memset or synchronisation), so it may be captured
+ * into a HIP graph; the captured graph keeps the pointers it was captured with. */
 pisa_status pisa_forward(pisa_plan_t *plan, const void *Q, const void *K, const void *V, void *out,
                          hipStream_t stream);
 

@@ -248,6 +248,41 @@ def test_two_plans_on_side_streams():
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
+def test_graph_capture_replays():
+    # pisa_forward launches kernels only (no allocation, no memset), so it can be captured in a
+    # HIP graph. Each replay follows eager work that changes Q in place, and must match an eager
+    # forward of a second plan on the same inputs bit for bit.
+    from sparse_attention_diffusion_pool_amd import _lib as L
+    w = custom("bf16-graph", 2, (7, 11, 13), 128, 128, 0.3, "bf16")
+    dev = torch.device("cuda", 0)
+    qd, kd, vd = (t.to(dev) for t in layer_inputs(w))
+    H, Lq, d = qd.shape
+    plan_g, plan_e = (L.Plan(Lq, H, d, w.B, w.keep, dtype=L.DTYPE_BF16) for _ in range(2))
+    plan_g.attach_workspace(device=dev)
+    plan_e.attach_workspace(device=dev)
+    out_g, ref = torch.empty_like(qd), torch.empty_like(qd)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan_g.forward(qd, kd, vd, out_g)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan_g.forward(qd, kd, vd, out_g)
+    torch.cuda.synchronize()
+    for r in range(4):
+        qd.mul_(1.0 + 0.25 * r)  # eager work between replays
+        plan_e.forward(qd, kd, vd, ref)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(ref.float()).all()
+        assert torch.equal(out_g, ref), f"replay {r} differs from the eager forward"
+    del graph
+    plan_g.destroy()
+    plan_e.destroy()
+
+
 def test_outputs_untouched_outside_rows_and_no_nan():
     # out is pre-filled with NaN by gpu_run: every row must be written, none left NaN
     w = custom("fill", 2, (7, 11, 13), 128, 128, 0.3, "bf16")
