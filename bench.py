@@ -434,7 +434,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=3, help="index into workloads.CONFIGS")
+    ap.add_argument("--workload", default="wan720p-like-L75600", help="workload name (workloads.WORKLOADS)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quality", action="store_true")
     ap.add_argument("--no-context", action="store_true",
@@ -492,27 +492,27 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build runs on a single MI355X and has no multi-GPU "
-              "path (heads would shard across GPUs with no exchange); run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: libpisa runs on a single MI355X and has no multi-GPU path "
+              "(heads would shard across GPUs with no exchange); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     if args.modes:
-        from workloads import CONFIGS
-        compare_modes(CONFIGS[args.workload], args.steps, args.warmup)
+        from workloads import workload
+        compare_modes(workload(args.workload), args.steps, args.warmup)
         return
     if args.sweep:
         latency_sweep(args.sweep_heads, args.steps, args.warmup)
         return
     if args.routing_quality:
-        from workloads import CONFIGS
-        routing_quality(CONFIGS[args.workload], args.sharpen, args.steps, args.warmup)
+        from workloads import workload
+        routing_quality(workload(args.workload), args.sharpen, args.steps, args.warmup)
         return
 
     import torch
     from sparse_attention_diffusion_pool_amd import _lib as L
-    from workloads import CONFIGS, layer_inputs
+    from workloads import layer_inputs, workload
 
-    w = CONFIGS[args.workload]
+    w = workload(args.workload)
     t_gen = time.perf_counter()
     q, k, v = layer_inputs(w)
     t_gen = time.perf_counter() - t_gen

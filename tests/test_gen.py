@@ -5,19 +5,19 @@ import math
 import numpy as np
 import torch
 
-from workloads import CONFIGS, custom, head_inputs, layer_inputs, to_float64
+from workloads import WORKLOADS, custom, head_inputs, layer_inputs, to_float64, workload
 
 
 def test_config_shapes():
     want = {0: (2, 1024, 64, 64, "f32"), 1: (24, 4608, 128, 64, "bf16"),
             2: (40, 32760, 128, 128, "bf16"), 3: (40, 75600, 128, 128, "bf16"),
             4: (24, 119056, 128, 128, "bf16")}
-    for w in CONFIGS:
+    for w in WORKLOADS:
         assert (w.H, w.L, w.d, w.B, w.dtype) == want[w.cfg_id]
 
 
 def test_reproducible_and_head_independent():
-    w = CONFIGS[0]
+    w = workload("tiny-2d-L1024")
     a = head_inputs(w, 1)
     b = head_inputs(custom("other", 1, (4, 4), 8, 4, 0.5, "f32"), 0)  # evict the cache
     c = head_inputs(w, 1)
@@ -52,7 +52,7 @@ def test_text_tokens_at_tail_iid():
 
 
 def test_flux_calibration_std():
-    w = CONFIGS[1]
+    w = workload("flux-like-L4608")
     q, k, _ = head_inputs(w, 3)
     qg, kg = to_float64(q[: w.n_grid]), to_float64(k[: w.n_grid])
     rng = np.random.default_rng(0)

@@ -11,7 +11,7 @@ import torch
 
 from pisa_cases import (assert_close, check_stats, compare_rows, gpu_run, log, oracle_head,
                         sample_blocks)
-from workloads import CONFIGS, custom, layer_inputs
+from workloads import custom, layer_inputs, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +35,7 @@ def _full_check(res, heads=None, label="", query_blocks=None, stats=True):
 # ---------------------------------------------------------------------------------------------
 
 def test_tiny_fp32_layer():
-    w = CONFIGS[0]
+    w = workload("tiny-2d-L1024")
     res = gpu_run(w, want_stats=True)
     _full_check(res, label=w.name)
 
@@ -43,7 +43,7 @@ def test_tiny_fp32_layer():
 @pytest.mark.parametrize("routing", [0, 1])
 @pytest.mark.parametrize("phases", [7, 3, 1])
 def test_tiny_fp32_modes(routing, phases):
-    w = CONFIGS[0]
+    w = workload("tiny-2d-L1024")
     res = gpu_run(w, routing=routing, phases=phases, want_stats=True)
     _full_check(res, label=f"{w.name} routing={routing} phases={phases}")
 
@@ -123,7 +123,7 @@ def test_block_first_order_inactive_without_first_phase():
 
 
 def test_block_first_order_wan720p():
-    w = CONFIGS[3]
+    w = workload("wan720p-like-L75600")
     res = gpu_run(w, heads=[0, 17], first_order=1)
     qb = sample_blocks(res["info"]["n_blocks"], 6, seed=31)
     _full_check(res, label=f"{w.name} block first order", query_blocks=qb, stats=False)
@@ -134,7 +134,7 @@ def test_block_first_order_wan720p():
 # ---------------------------------------------------------------------------------------------
 
 def test_tiny_fp32_spectral():
-    w = CONFIGS[0]
+    w = workload("tiny-2d-L1024")
     res = gpu_run(w, want_stats=True, norm=1)
     _full_check(res, label=f"{w.name} spectral")
 
@@ -149,7 +149,7 @@ def test_small_spectral(case):
 
 
 def test_spectral_wan720p_selection():
-    w = CONFIGS[3]
+    w = workload("wan720p-like-L75600")
     res = gpu_run(w, heads=[0, 29], want_stats=True, norm=1)
     qb = sample_blocks(res["info"]["n_blocks"], 6, seed=7)
     _full_check(res, label=f"{w.name} spectral", query_blocks=qb)
@@ -160,7 +160,7 @@ def test_spectral_wan720p_selection():
 # ---------------------------------------------------------------------------------------------
 
 def test_flux_like_layer():
-    w = CONFIGS[1]
+    w = workload("flux-like-L4608")
     res = gpu_run(w, want_stats=True)
     H = w.H
     for h in range(H):
@@ -175,13 +175,13 @@ def test_flux_like_layer():
 # selection and statistics, outputs on sampled query blocks (first, last/ragged, random).
 # ---------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("cfg", [2, 3, 4])
-def test_full_size_layers(cfg):
-    w = CONFIGS[cfg]
+@pytest.mark.parametrize("name", ["wan480p-like-L32760", "wan720p-like-L75600", "hunyuan720p-like-L119056"])
+def test_full_size_layers(name):
+    w = workload(name)
     res = gpu_run(w, want_stats=True)
     nb = res["info"]["n_blocks"]
     heads = [0, w.H // 2, w.H - 1]
-    qb = sample_blocks(nb, 10, seed=cfg)
+    qb = sample_blocks(nb, 10, seed=w.cfg_id)
     _full_check(res, heads=heads, label=w.name, query_blocks=qb)
 
 
@@ -213,7 +213,7 @@ def test_large_block_counts(case):
 # ---------------------------------------------------------------------------------------------
 
 def test_deterministic_and_stages_match_forward():
-    w = CONFIGS[1]
+    w = workload("flux-like-L4608")
     inputs = layer_inputs(w, heads=range(6))
     a = gpu_run(w, inputs=inputs)
     b = gpu_run(w, inputs=inputs)

@@ -14,7 +14,7 @@ import torch.nn.functional as F
 
 from oracle import brute
 from oracle import pisa_oracle as po
-from workloads import CONFIGS, custom, head_inputs, to_float64
+from workloads import custom, head_inputs, to_float64, workload
 
 
 def _sdpa(q, k, v, scale, mask=None):
@@ -44,7 +44,7 @@ def test_keep_all_equals_dense(L, d, B):
 
 
 def test_keep_all_equals_dense_tiny_config():
-    w = CONFIGS[0]
+    w = workload("tiny-2d-L1024")
     q, k, v = (to_float64(t) for t in head_inputs(w, 0))
     r = po.pisa_head(q, k, v, w.B, keep=1.0)
     ref = _sdpa(q, k, v, 1.0 / math.sqrt(w.d))
@@ -204,7 +204,7 @@ def test_spectral_equals_frobenius_for_rank_one():
 # --- P6: H-bar identity from whole-matrix products ------------------------------------------------
 
 def test_hbar_identity():
-    w = CONFIGS[0]
+    w = workload("tiny-2d-L1024")
     q, k, v = (to_float64(t) for t in head_inputs(w, 1))
     st = po.head_stats(q, k, v, w.B, 1 / math.sqrt(w.d))
     nb = po.n_blocks(w.L, w.B)
@@ -277,7 +277,7 @@ def test_key_translation():
 # --- P10: plain routing is the textbook top-k of the pooled product; ties go to the lower index ---
 
 def test_plain_routing_is_topk():
-    w = CONFIGS[0]
+    w = workload("tiny-2d-L1024")
     q, k, v = (to_float64(t) for t in head_inputs(w, 0))
     tau = 1 / math.sqrt(w.d)
     r = po.pisa_head(q, k, v, w.B, w.keep, routing="plain")

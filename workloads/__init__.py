@@ -4,4 +4,4 @@ This package synthesises Q, K and V only. It holds none of the attention method'
 (no block statistics, no scores, no selection, no softmax).
 """
 
-from .gen import CONFIGS, Workload, custom, head_inputs, layer_inputs, to_float64  # noqa: F401
+from .gen import WORKLOADS, Workload, custom, workload, head_inputs, layer_inputs, to_float64  # noqa: F401

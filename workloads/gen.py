@@ -36,7 +36,7 @@ from typing import Iterable, Optional, Sequence, Tuple
 import numpy as np
 import torch
 
-__all__ = ["Workload", "CONFIGS", "custom", "head_inputs", "layer_inputs", "to_float64"]
+__all__ = ["Workload", "WORKLOADS", "workload", "custom", "head_inputs", "layer_inputs", "to_float64"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -84,7 +84,7 @@ class Workload:
 
 # The five synthetic attention layers: tiny CPU-checkable, FLUX-like image, Wan2.1-14B-like 480p
 # and 720p video, Hunyuan-Video-like 720p video with text.
-CONFIGS: Sequence[Workload] = (
+WORKLOADS: Sequence[Workload] = (
     Workload(0, "tiny-2d-L1024", H=2, grid=(32, 32), n_text=0, d=64, B=64, keep=0.25,
              dtype="f32", n_freq=16),
     Workload(1, "flux-like-L4608", H=24, grid=(64, 64), n_text=512, d=128, B=64, keep=0.25,
@@ -97,6 +97,14 @@ CONFIGS: Sequence[Workload] = (
              keep=0.08, dtype="bf16", n_freq=32),
 )
 
+
+
+def workload(name: str) -> Workload:
+    """The synthetic layer of that name (see WORKLOADS)."""
+    for w in WORKLOADS:
+        if w.name == name:
+            return w
+    raise KeyError(f"unknown workload {name!r}; known: {', '.join(w.name for w in WORKLOADS)}")
 
 def custom(name: str, H: int, grid: Sequence[int], d: int, B: int, keep: float, dtype: str,
            n_text: int = 0, n_freq: Optional[int] = None, calib_std: Optional[float] = None,
