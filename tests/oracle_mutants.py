@@ -120,6 +120,33 @@ def routing_no_log(po):
     po.routing_scores = routing_scores
 
 
+def _cov_term_mutant(po, term):
+    orig = po.routing_scores
+
+    def routing_scores(st, routing="cov"):
+        if routing != "cov":
+            return orig(st, routing)
+        qn = np.sqrt(np.einsum("id,id->i", st.qbar, st.qbar))
+        return st.qbar @ st.kbar.T + term(st.n[None, :], qn[:, None], st.M[None, :], st.qbar.shape[1])
+
+    po.routing_scores = routing_scores
+
+
+def routing_qnorm_unscaled(po):
+    """Covariance term weighted by the norm of the unscaled pooled query (softmax scale 1/sqrt(d))."""
+    _cov_term_mutant(po, lambda n, qn, M, d: np.log(n + qn * math.sqrt(d) * M))
+
+
+def routing_no_count(po):
+    """Covariance term without the block's row count: ln(|qbar| M_j)."""
+    _cov_term_mutant(po, lambda n, qn, M, d: np.log(qn * M))
+
+
+def routing_no_qnorm(po):
+    """Covariance term without the pooled-query weight: ln(n_j + M_j)."""
+    _cov_term_mutant(po, lambda n, qn, M, d: np.log(n + M))
+
+
 def ties_to_higher_index(po):
     """Equal scores broken towards the larger block index."""
     def select_blocks(scores, k):
@@ -150,7 +177,8 @@ def last_block_short(po):
 MUTANTS = {f.__name__: f for f in (
     no_first_order, hbar_transposed, hbar_summed, h_not_centred, m_not_centred, qbar_unscaled,
     vmean_for_vsum, ragged_counted_full, denominator_without_counts, exact_scores_unscaled,
-    routing_sign, routing_no_log, ties_to_higher_index, k_rounded_down, last_block_short)}
+    routing_sign, routing_no_log, routing_qnorm_unscaled, routing_no_count, routing_no_qnorm,
+    ties_to_higher_index, k_rounded_down, last_block_short)}
 
 
 def apply(name: str) -> None:

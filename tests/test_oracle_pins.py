@@ -94,6 +94,75 @@ def test_cov_routing_reduces_to_plain_when_blocks_are_homogeneous():
     assert all(np.array_equal(x, y) for x, y in zip(a, b))
 
 
+# --- covariance-aware routing term (gist.science summary, section 2 "Covariance-aware routing") ----
+# The pages name the score's ingredients (the attention score and M_j = ||H_j - H-bar||) without a
+# formula; the reading ranks block j by its zeroth-order mass n_j alpha plus the bound
+# alpha ||q~|| M_j on the first-order numerator error, in logs at the pooled query. The three pins
+# below each isolate one ingredient with quantities computed outside the oracle.
+
+def test_cov_minus_plain_is_log_count_with_flat_blocks():
+    # keys constant inside every block: H_j = 0 = H-bar, M_j = 0, so the covariance term is ln n_j,
+    # with n_j = B for full blocks and L - (N_b - 1) B for the ragged last one
+    L, d, B = 150, 8, 16
+    rng = np.random.default_rng(41)
+    nb = -(-L // B)
+    q = 0.7 + rng.standard_normal((L, d))
+    v = rng.standard_normal((L, d))
+    k = np.repeat(rng.standard_normal((nb, d)), B, axis=0)[:L]
+    st = po.head_stats(q, k, v, B, 1 / math.sqrt(d))
+    gap = po.routing_scores(st, "cov") - po.routing_scores(st, "plain")
+    counts = np.array([B] * (nb - 1) + [L - (nb - 1) * B], dtype=np.float64)
+    assert counts[-1] == 6
+    assert np.max(np.abs(gap - np.log(counts)[None, :])) < 1e-12
+
+
+def _equal_centroid_layer(seed=43):
+    # blocks 0 and 1 share their centroid c; block 0's keys spread along its values (large H_0),
+    # block 1's keys are all c (H_1 = 0); blocks 2..4 are random, block 4 ragged
+    L, d, B = 72, 8, 16
+    rng = np.random.default_rng(seed)
+    q = 1.0 + rng.standard_normal((L, d))
+    v = rng.standard_normal((L, d))
+    k = rng.standard_normal((L, d))
+    c = rng.standard_normal(d)
+    spread = 3.0 * v[0:B, :d]
+    spread -= spread.mean(axis=0)
+    k[0:B] = c + spread
+    k[B:2 * B] = c
+    return q, k, v, B, 1 / math.sqrt(d)
+
+
+def test_cov_score_gap_between_equal_centroids():
+    # equal q.kbar: the score gap is the covariance term alone, ln((n + |qbar_i| M_0)/(n + |qbar_i| M_1)),
+    # with |qbar_i| the Euclidean norm of the scaled pooled query (taken here from q directly) and
+    # M_j from the element loops; the block with the larger M_j ranks higher in every row
+    q, k, v, B, tau = _equal_centroid_layer()
+    L, d = q.shape
+    st = po.head_stats(q, k, v, B, tau)
+    sc = po.routing_scores(st, "cov")
+    bs = brute.block_stats(*_lists(q, k, v), B, tau)
+    M0, M1 = bs["M"][0], bs["M"][1]
+    assert M0 > 2 * M1 > 0
+    for i, (s0, e0) in enumerate(po.block_bounds(L, B)):
+        qn = math.sqrt(sum((tau * sum(q[r][c] for r in range(s0, e0)) / (e0 - s0)) ** 2 for c in range(d)))
+        want = math.log((B + qn * M0) / (B + qn * M1))
+        assert abs((sc[i, 0] - sc[i, 1]) - want) < 1e-10
+        assert sc[i, 0] > sc[i, 1]
+
+
+@pytest.mark.parametrize("norm", ["fro", "spectral"])
+def test_cov_m_bounds_first_order_error(norm):
+    # M_j bounds the first-order numerator error of routing j to U at any query:
+    # |q (H_j - H-bar)| <= |q| M_j, for the pooled queries and for every token's scaled query
+    q, k, v, B, tau = _equal_centroid_layer(seed=47)
+    st = po.head_stats(q, k, v, B, tau, norm=norm)
+    bs = brute.block_stats(*_lists(q, k, v), B, tau)
+    E = np.array(bs["H"]) - np.array(bs["Hbar"])[None]
+    for x in list(st.qbar) + list(tau * q):
+        lhs = np.linalg.norm(np.einsum("a,jab->jb", x, E), axis=1)
+        assert np.all(lhs <= np.linalg.norm(x) * st.M * (1 + 1e-12) + 1e-12)
+
+
 # --- P4: the centroid is the mean, so the denominator's first-order sum vanishes -----------------
 
 def test_denominator_first_order_vanishes():
