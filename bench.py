@@ -100,7 +100,19 @@ def cpu_baseline(w, heads, sample_note):
         f = po.executed_flops(w.L, w.d, w.B, r["S"])
         flops += f["total"]
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": sample_note, "seconds": secs, "cpu": platform.processor() or platform.machine()}
+            "sample": sample_note, "seconds": secs, "cpu": cpu_model()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 KERNELS = ("stats_pass_bf16", "stats_cov_bf16", "stats_finalize", "stats_f32", "route_kernel", "attend_bf16", "mfma_probe",
@@ -539,6 +551,7 @@ def main():
     attend_tflops = fl["attend"] / (attend_ms.mean() * 1e-3) / 1e12
     stats_gbps = info["bytes_stats"] / (stats_ms.mean() * 1e-3) / 1e9
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_VALU_TFLOPS
+    esize = 2 if w.dtype == "bf16" else 4
 
     traffic = None
     default_mode = args.phases == 7 and args.routing == "cov" and args.norm == "fro" and first_order == 0
@@ -574,7 +587,10 @@ def main():
         "roofline": {"kernel": "attend_bf16" if w.dtype == "bf16" else "attend_f32",
                      "bound": "mfma" if w.dtype == "bf16" else "alu",
                      "achieved": round(attend_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(attend_tflops / peak, 4), "traffic": traffic},
+                     "frac": round(attend_tflops / peak, 4), "traffic": traffic,
+                     # HBM-side bytes over the compulsory Q, K, V reads and out write of one launch
+                     "traffic_ratio": (round(traffic / (4.0 * w.H * w.L * w.d * esize), 2)
+                                       if traffic is not None else None)},
     }
 
     if w.dtype == "bf16" and args.phases == 7 and not args.no_context:

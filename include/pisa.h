@@ -31,8 +31,10 @@
  * (its workspace) must not be used by two calls that can run concurrently.
  *
  * Errors: every call returns a pisa_status and never aborts. Argument errors are reported before
- * any launch; a failed launch or missing device returns PISA_ERR_DEVICE. pisa_last_error() gives
- * the calling thread's last error text.
+ * any launch: NULL, misaligned or overlapping pointers first (no HIP call), then, once a device is
+ * present, any of Q, K, V, out or the workspace that is not device memory (a host address) or
+ * whose extent runs past the end of its allocation. A failed launch or missing device returns
+ * PISA_ERR_DEVICE. pisa_last_error() gives the calling thread's last error text.
  *
  * Supported: dtype bf16 with d = 128, B in {64, 128}; dtype fp32 with d in {64, 128},
  * B in {64, 128}; L >= 1, H >= 1, 0 < keep <= 1, H * L * d < 2^31 elements per tensor;
@@ -43,6 +45,11 @@
 
 #include <stddef.h>
 #include <stdint.h>
+/* hipStream_t comes from the HIP runtime header, which needs its platform named; a C or C++
+ * consumer compiled without hipcc (gcc, clang) gets the AMD platform here. */
+#ifndef __HIP_PLATFORM_AMD__
+#define __HIP_PLATFORM_AMD__ 1
+#endif
 #include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
@@ -71,7 +78,9 @@ typedef enum pisa_option {
 
 enum { PISA_DTYPE_BF16 = 0, PISA_DTYPE_F32 = 1 };
 enum { PISA_ROUTING_COV = 0, PISA_ROUTING_PLAIN = 1 };
-/* PHASES = EXACT alone is keep-or-drop block-sparse attention; EXACT|ZEROTH omits H-bar. */
+/* PHASES = EXACT alone is keep-or-drop block-sparse attention; EXACT|ZEROTH omits H-bar.
+ * FIRST needs ZEROTH (beta_t, the first-order weight, is the sum of the zeroth-order alpha_{t,j}):
+ * the masks accepted are 1, 3 and 7; any other gives PISA_ERR_INVALID_ARGUMENT. */
 enum { PISA_PHASE_EXACT = 1, PISA_PHASE_ZEROTH = 2, PISA_PHASE_FIRST = 4 };
 /* First-order term of the unselected blocks. GLOBAL is the method: beta_t (q~_t H-bar), one
  * shared d x d matrix. BLOCK is the variant the method replaces (gist.science section 2 "Core
@@ -104,7 +113,12 @@ typedef struct pisa_plan_info {
 } pisa_plan_info_t;
 
 /* Create a plan for H heads of L tokens, head dim d, block size B, keeping a fraction `keep` of
- * the N_b key/value blocks per query block. Host only. */
+ * the N_b key/value blocks per query block. The partition follows the AI Radio episode's paper
+ * summary (queries, keys and values cut into blocks of size B; query block i keeps a critical set
+ * S_i and approximates the rest, U_i); k = clamp(ceil(keep N_b - 1e-9), 1, N_b) blocks are kept.
+ * Host only (no HIP call). *plan is set to NULL on error. Errors: INVALID_ARGUMENT for L, H, d or
+ * B < 1, keep outside (0, 1] or a NULL plan pointer; UNSUPPORTED for sizes outside the list
+ * above. */
 pisa_status pisa_plan(int64_t L, int32_t H, int32_t d, int32_t B, double keep, pisa_plan_t **plan);
 
 /* Set an option (see pisa_option). Changing the dtype, or selecting the block-wise first-order
@@ -118,10 +132,14 @@ pisa_status pisa_plan_info(const pisa_plan_t *plan, pisa_plan_info_t *info);
  * plan keeps the pointer, not ownership. */
 pisa_status pisa_plan_attach_workspace(pisa_plan_t *plan, void *dev_ptr, size_t bytes);
 
-/* The whole forward pass: statistics, routing, fused piecewise attention. Enqueued on `stream`
- * (asynchronous). Equivalent to pisa_forward_stats + pisa_forward_route + pisa_forward_attend.
- * It only launches kernels (no allocation, memset or synchronisation), so it may be captured
- * into a HIP graph; the captured graph keeps the pointers it was captured with. */
+/* The whole forward pass: statistics, routing, fused piecewise attention, o_t = N_t / D_t for
+ * every row (gist.science summary, section 2 "Core algorithm" for N_t, D_t and alpha; "Hardware
+ * implementation" for the precompute and the three phases). Q, K, V: device [H, L, d] inputs,
+ * read only; out: device [H, L, d], written in full. Enqueued on `stream` (asynchronous).
+ * Equivalent to pisa_forward_stats + pisa_forward_route + pisa_forward_attend, with the argument
+ * checks done once. It only launches kernels (no allocation, memset or synchronisation), so it
+ * may be captured into a HIP graph; the captured graph keeps the pointers it was captured with.
+ * Errors: INVALID_HANDLE, WORKSPACE, INVALID_ARGUMENT (see "Errors" above), DEVICE. */
 pisa_status pisa_forward(pisa_plan_t *plan, const void *Q, const void *K, const void *V, void *out,
                          hipStream_t stream);
 

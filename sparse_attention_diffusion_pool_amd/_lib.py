@@ -119,8 +119,34 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
+def _tensor_ptr(t, name: str, info: dict) -> int:
+    """Address of a Q/K/V/out argument. A torch tensor must have the plan's dtype, shape [H, L, d],
+    be contiguous and live on the GPU; anything else raises here, before the library is called (a
+    transposed [L, H, d] -> [H, L, d] view would otherwise be read with the wrong strides, and a host
+    tensor's address would reach the kernels). Raw integer addresses are passed through: the library
+    checks that they point into device memory large enough for the tensor."""
+    if t is None or isinstance(t, int):
+        return t
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor or a device address, got {type(t).__name__}")
+    want = torch.bfloat16 if info["dtype"] == DTYPE_BF16 else torch.float32
+    if t.dtype != want:
+        raise TypeError(f"{name}: dtype {t.dtype}, the plan computes in {want}")
+    shape = (info["H"], info["L"], info["d"])
+    if tuple(t.shape) != shape:
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, the plan expects [H, L, d] = {list(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: not contiguous (strides {t.stride()}); a transposed view needs "
+                         ".contiguous() first")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: on {t.device}, the library reads device memory")
+    return t.data_ptr()
+
+
 class Plan:
-    """A libpisa plan. Tensors are passed as torch tensors (device memory) or raw addresses."""
+    """A libpisa plan. Tensors are passed as torch tensors (device memory, the plan's dtype, shape
+    [H, L, d], contiguous; checked before the call) or raw device addresses."""
 
     def __init__(self, L: int, H: int, d: int, B: int, keep: float, dtype=None, scale=None,
                  routing=None, phases=None, first_order=None, norm=None):
@@ -154,19 +180,25 @@ class Plan:
         self._ws = ws
         return ws
 
+    def _args(self, **tensors):
+        info = self.info()
+        return [_tensor_ptr(t, name, info) for name, t in tensors.items()]
+
     def forward(self, Q, K, V, out, stream=None):
-        check(load().pisa_forward(self._h, _ptr(Q), _ptr(K), _ptr(V), _ptr(out), _stream(stream)), "pisa_forward")
+        q, k, v, o = self._args(Q=Q, K=K, V=V, out=out)
+        check(load().pisa_forward(self._h, q, k, v, o, _stream(stream)), "pisa_forward")
         return out
 
     def forward_stats(self, Q, K, V, stream=None):
-        check(load().pisa_forward_stats(self._h, _ptr(Q), _ptr(K), _ptr(V), _stream(stream)), "pisa_forward_stats")
+        q, k, v = self._args(Q=Q, K=K, V=V)
+        check(load().pisa_forward_stats(self._h, q, k, v, _stream(stream)), "pisa_forward_stats")
 
     def forward_route(self, stream=None):
         check(load().pisa_forward_route(self._h, _stream(stream)), "pisa_forward_route")
 
     def forward_attend(self, Q, K, V, out, stream=None):
-        check(load().pisa_forward_attend(self._h, _ptr(Q), _ptr(K), _ptr(V), _ptr(out), _stream(stream)),
-              "pisa_forward_attend")
+        q, k, v, o = self._args(Q=Q, K=K, V=V, out=out)
+        check(load().pisa_forward_attend(self._h, q, k, v, o, _stream(stream)), "pisa_forward_attend")
         return out
 
     def debug_copy_stats(self, qbar=None, kbar=None, vsum=None, hbar=None, M=None, stream=None):

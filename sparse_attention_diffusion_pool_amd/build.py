@@ -56,5 +56,33 @@ def build(verbose: bool = False, jobs: int = 8, extra=()) -> str:
     return OUT
 
 
+def build_host_sanitized() -> str:
+    """A copy of libpisa whose host layer (pisa_host.cpp: plans, argument checks, dispatch) is
+    built by g++ with AddressSanitizer and UndefinedBehaviorSanitizer, linked with the kernels'
+    objects from ``build()``. For CPU-side checks of the C ABI (the GPU code is not instrumented).
+    Loading it needs the ASan runtime preloaded (``gcc -print-file-name=libasan.so``)."""
+    bdir = os.path.join(PKG, "_build")
+    sdir = os.path.join(bdir, "asan")
+    os.makedirs(sdir, exist_ok=True)
+    dev_objs = [os.path.join(bdir, os.path.splitext(s)[0] + ".o") for s in SOURCES if s.endswith(".hip")]
+    if not all(os.path.exists(o) for o in dev_objs):
+        build()
+    gxx = shutil.which("g++") or "g++"
+    san = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=undefined"]
+    host_obj = os.path.join(sdir, "pisa_host.o")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fPIC", "-D__HIP_PLATFORM_AMD__", "-isystem", "/opt/rocm/include",
+           f"-I{os.path.join(ROOT, 'include')}", *san, "-c", os.path.join(CSRC, "pisa_host.cpp"), "-o", host_obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"g++ failed:\n{' '.join(cmd)}\n{r.stderr}")
+    out = os.path.join(sdir, "libpisa_asan.so")
+    cmd = [gxx, "-shared", *san, "-o", out, host_obj, *dev_objs, "-L/opt/rocm/lib", "-lamdhip64",
+           "-Wl,-rpath,/opt/rocm/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stderr}")
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

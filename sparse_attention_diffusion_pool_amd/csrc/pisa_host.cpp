@@ -157,6 +157,32 @@ pisa_status check_device() {
   return PISA_OK;
 }
 
+// `bytes` from ptr must be device memory of one allocation. A host address, or a range that runs
+// past the end of its allocation, would fault the kernels; it is rejected here instead. A failed
+// query leaves no error behind for the launch checks that follow (hipGetLastError clears it).
+pisa_status check_device_memory(const void* ptr, size_t bytes, const char* name) {
+  hipPointerAttribute_t a{};
+  hipError_t e = hipPointerGetAttributes(&a, ptr);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PISA_ERR_INVALID_ARGUMENT, "%s (%p) is not device memory (%s)", name, ptr, hipGetErrorString(e));
+  }
+  if (a.type != hipMemoryTypeDevice && a.type != hipMemoryTypeManaged)
+    return fail(PISA_ERR_INVALID_ARGUMENT, "%s (%p) is not device memory (memory type %d)", name, ptr, (int)a.type);
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  e = hipMemGetAddressRange(&base, &size, const_cast<void*>(ptr));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return PISA_OK;  // the range query is not available for every allocation kind
+  }
+  const size_t left = size - (size_t)(static_cast<const char*>(ptr) - static_cast<const char*>(base));
+  if (bytes > left)
+    return fail(PISA_ERR_INVALID_ARGUMENT, "%s: %zu bytes needed from %p, but its allocation ends after %zu",
+                name, bytes, ptr, left);
+  return PISA_OK;
+}
+
 pisa_status check_ready(pisa_plan_t* p) {
   if (!valid_plan(p)) return fail(PISA_ERR_INVALID_HANDLE, "invalid or destroyed plan");
   if (p->ws == nullptr) return fail(PISA_ERR_WORKSPACE, "no workspace attached");
@@ -189,13 +215,87 @@ pisa_status check_tensors(const pisa_plan_t* p, const void* Q, const void* K, co
   return PISA_OK;
 }
 
+// PISA_DEBUG_SYNC set in the environment: synchronise after every launch and report the kernel
+// that failed (read once per process).
+bool debug_sync() {
+  static const bool on = getenv("PISA_DEBUG_SYNC") != nullptr;
+  return on;
+}
+
 pisa_status launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(PISA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
-  if (getenv("PISA_DEBUG_SYNC") != nullptr) {
+  if (debug_sync()) {
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return fail(PISA_ERR_DEVICE, "%s (synchronised): %s", what, hipGetErrorString(e));
   }
   return PISA_OK;
+}
+
+pisa_status check_inputs_resident(const pisa_plan_t* p, const void* Q, const void* K, const void* V,
+                                  const void* out);
+
+// What a call reads and writes besides the workspace.
+enum Uses { kWorkspaceOnly, kInputs, kInputsAndOut };
+
+// Every check of a call that touches device memory, once per call: plan, workspace, pointer
+// arguments (NULL, alignment, overlap), device present, and each buffer resident in device memory
+// with room for its extent.
+pisa_status prepare(pisa_plan_t* p, const void* Q, const void* K, const void* V, const void* out, Uses uses) {
+  pisa_status s = check_ready(p);
+  if (s != PISA_OK) return s;
+  if (uses == kInputsAndOut && out == nullptr) return fail(PISA_ERR_INVALID_ARGUMENT, "out is NULL");
+  const bool tensors = uses != kWorkspaceOnly;
+  if (tensors && (s = check_tensors(p, Q, K, V, out)) != PISA_OK) return s;
+  if ((s = check_device()) != PISA_OK) return s;
+  if ((s = check_device_memory(p->ws, pisa::workspace_layout(p->dm).total, "workspace")) != PISA_OK) return s;
+  return tensors ? check_inputs_resident(p, Q, K, V, out) : PISA_OK;
+}
+
+// Q, K, V (and out, when given) in device memory with room for [H, L, d] each.
+pisa_status check_inputs_resident(const pisa_plan_t* p, const void* Q, const void* K, const void* V,
+                                  const void* out) {
+  const pisa::Dims& dm = p->dm;
+  pisa_status s;
+  const size_t bytes = (size_t)dm.H * dm.L * dm.d * (dm.dtype == PISA_DTYPE_BF16 ? 2 : 4);
+  const void* ptrs[4] = {Q, K, V, out};
+  const char* names[4] = {"Q", "K", "V", "out"};
+  for (int i = 0; i < 4; ++i)
+    if (ptrs[i] != nullptr && (s = check_device_memory(ptrs[i], bytes, names[i])) != PISA_OK) return s;
+  return PISA_OK;
+}
+
+// The stages' launches, on a plan and arguments that prepare() accepted.
+pisa_status run_stats(pisa_plan_t* p, void* ws, const void* Q, const void* K, const void* V, hipStream_t stream) {
+  pisa::Work w = pisa::workspace_pointers(p->dm, ws);
+  pisa_status s;
+  if ((s = launched(pisa::launch_stats_pass(p->dm, w, Q, K, V, stream), "stats pass")) != PISA_OK) return s;
+  if ((s = launched(pisa::launch_stats_finalize(p->dm, w, stream), "H-bar finalize")) != PISA_OK) return s;
+  if (p->dm.routing == PISA_ROUTING_COV || pisa::block_first_order(p->dm))
+    return launched(pisa::launch_stats_cov(p->dm, w, K, V, stream), "block covariance norms");
+  return PISA_OK;
+}
+
+pisa_status run_route(pisa_plan_t* p, void* ws, hipStream_t stream) {
+  pisa::Work w = pisa::workspace_pointers(p->dm, ws);
+  return launched(pisa::launch_route(p->dm, w, stream), "route");
+}
+
+pisa_status run_attend(pisa_plan_t* p, void* ws, const void* Q, const void* K, const void* V, void* out,
+                       hipStream_t stream) {
+  pisa::Work w = pisa::workspace_pointers(p->dm, ws);
+  pisa_status s;
+  if ((s = launched(pisa::launch_attend(p->dm, w, Q, K, V, out, stream), "attend")) != PISA_OK) return s;
+  if (pisa::block_first_order(p->dm))
+    return launched(pisa::launch_first_block_bf16(p->dm, w, Q, out, stream), "block first order");
+  return PISA_OK;
+}
+
+pisa_status run_forward(pisa_plan_t* p, void* ws, const void* Q, const void* K, const void* V, void* out,
+                        hipStream_t stream) {
+  pisa_status s;
+  if ((s = run_stats(p, ws, Q, K, V, stream)) != PISA_OK) return s;
+  if ((s = run_route(p, ws, stream)) != PISA_OK) return s;
+  return run_attend(p, ws, Q, K, V, out, stream);
 }
 
 }  // namespace
@@ -259,6 +359,10 @@ pisa_status pisa_plan_set(pisa_plan_t* p, pisa_option opt, double value) {
       int m = (int)value;
       if ((double)m != value || m < 1 || m > 7 || !(m & PISA_PHASE_EXACT))
         return fail(PISA_ERR_INVALID_ARGUMENT, "phases must be a mask of PISA_PHASE_* including EXACT");
+      // beta_t, the weight of the first-order term, is the sum of the zeroth-order alpha_{t,j}:
+      // there is no first-order term without the zeroth-order one
+      if ((m & PISA_PHASE_FIRST) && !(m & PISA_PHASE_ZEROTH))
+        return fail(PISA_ERR_INVALID_ARGUMENT, "PISA_PHASE_FIRST needs PISA_PHASE_ZEROTH");
       dm.phases = m;
       break;
     }
@@ -324,49 +428,25 @@ pisa_status pisa_plan_attach_workspace(pisa_plan_t* p, void* dev_ptr, size_t byt
 }
 
 pisa_status pisa_forward_stats(pisa_plan_t* p, const void* Q, const void* K, const void* V, hipStream_t stream) {
-  pisa_status s = check_ready(p);
-  if (s != PISA_OK) return s;
-  if ((s = check_tensors(p, Q, K, V, nullptr)) != PISA_OK) return s;
-  if ((s = check_device()) != PISA_OK) return s;
-  pisa::Work w = pisa::workspace_pointers(p->dm, p->ws);
-  if ((s = launched(pisa::launch_stats_pass(p->dm, w, Q, K, V, stream), "stats pass")) != PISA_OK) return s;
-  if ((s = launched(pisa::launch_stats_finalize(p->dm, w, stream), "H-bar finalize")) != PISA_OK) return s;
-  if (p->dm.routing == PISA_ROUTING_COV || pisa::block_first_order(p->dm))
-    if ((s = launched(pisa::launch_stats_cov(p->dm, w, K, V, stream), "block covariance norms")) != PISA_OK) return s;
-  return PISA_OK;
+  pisa_status s = prepare(p, Q, K, V, nullptr, kInputs);
+  return s != PISA_OK ? s : run_stats(p, p->ws, Q, K, V, stream);
 }
 
 pisa_status pisa_forward_route(pisa_plan_t* p, hipStream_t stream) {
-  pisa_status s = check_ready(p);
-  if (s != PISA_OK) return s;
-  if ((s = check_device()) != PISA_OK) return s;
-  pisa::Work w = pisa::workspace_pointers(p->dm, p->ws);
-  return launched(pisa::launch_route(p->dm, w, stream), "route");
+  pisa_status s = prepare(p, nullptr, nullptr, nullptr, nullptr, kWorkspaceOnly);
+  return s != PISA_OK ? s : run_route(p, p->ws, stream);
 }
 
 pisa_status pisa_forward_attend(pisa_plan_t* p, const void* Q, const void* K, const void* V, void* out,
                                 hipStream_t stream) {
-  pisa_status s = check_ready(p);
-  if (s != PISA_OK) return s;
-  if (out == nullptr) return fail(PISA_ERR_INVALID_ARGUMENT, "out is NULL");
-  if ((s = check_tensors(p, Q, K, V, out)) != PISA_OK) return s;
-  if ((s = check_device()) != PISA_OK) return s;
-  pisa::Work w = pisa::workspace_pointers(p->dm, p->ws);
-  if ((s = launched(pisa::launch_attend(p->dm, w, Q, K, V, out, stream), "attend")) != PISA_OK) return s;
-  if (pisa::block_first_order(p->dm))
-    return launched(pisa::launch_first_block_bf16(p->dm, w, Q, out, stream), "block first order");
-  return PISA_OK;
+  pisa_status s = prepare(p, Q, K, V, out, kInputsAndOut);
+  return s != PISA_OK ? s : run_attend(p, p->ws, Q, K, V, out, stream);
 }
 
 pisa_status pisa_forward(pisa_plan_t* p, const void* Q, const void* K, const void* V, void* out, hipStream_t stream) {
-  pisa_status s = check_ready(p);
+  pisa_status s = prepare(p, Q, K, V, out, kInputsAndOut);
   if (s != PISA_OK) return s;
-  if (out == nullptr) return fail(PISA_ERR_INVALID_ARGUMENT, "out is NULL");
-  if ((s = check_tensors(p, Q, K, V, out)) != PISA_OK) return s;
-  if ((s = check_device()) != PISA_OK) return s;
-  if ((s = pisa_forward_stats(p, Q, K, V, stream)) != PISA_OK) return s;
-  if ((s = pisa_forward_route(p, stream)) != PISA_OK) return s;
-  return pisa_forward_attend(p, Q, K, V, out, stream);
+  return run_forward(p, p->ws, Q, K, V, out, stream);
 }
 
 pisa_status pisa_plan_destroy(pisa_plan_t* p) {

@@ -1,7 +1,7 @@
 // Internal interface between the C-ABI host layer (pisa_host.cpp) and the kernel launchers.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 

@@ -5,6 +5,7 @@ import ctypes
 import math
 import subprocess
 
+import numpy as np
 import pytest
 
 from oracle import pisa_oracle as po
@@ -176,3 +177,34 @@ def test_mfma_probe_argument_checks(lib):
     assert lib.pisa_debug_mfma_probe(1, 10, None, buf, None) == 1
     assert lib.pisa_debug_mfma_probe(1, 10, buf, None, None) == 1
     assert "NULL" in L.last_error()
+
+
+def test_phase_mask_first_needs_zeroth(lib):
+    # beta_t is the sum of the zeroth-order alpha_{t,j}: a first-order term without the zeroth-order
+    # one is undefined, and the mask that asks for it (EXACT | FIRST) is refused
+    p = L.Plan(1000, 2, 128, 128, 0.25)
+    for mask, status in ((5, 1), (4, 1), (6, 1), (1, 0), (3, 0), (7, 0)):
+        assert lib.pisa_plan_set(p.handle, L.OPT_PHASES, float(mask)) == status, mask
+    assert p.info()["phases"] == 7
+
+
+def test_binding_rejects_bad_tensors_before_the_call():
+    # the Python binding checks dtype, shape, contiguity and device before calling the library
+    import torch
+    H, Lq, d = 2, 1000, 128
+    p = L.Plan(Lq, H, d, 128, 0.25)
+    good = [torch.zeros((H, Lq, d), dtype=torch.bfloat16) for _ in range(4)]
+    with pytest.raises(ValueError, match="device memory"):
+        p.forward(*good)
+    with pytest.raises(TypeError, match="dtype"):
+        p.forward(good[0].float(), *good[1:])
+    with pytest.raises(ValueError, match="shape"):
+        p.forward(good[0][:, :999], *good[1:])
+    # the usual DiT layout [L, H, d] viewed as [H, L, d]
+    dit = torch.zeros((Lq, H, d), dtype=torch.bfloat16).transpose(0, 1)
+    with pytest.raises(ValueError, match="contiguous"):
+        p.forward(dit, *good[1:])
+    with pytest.raises(ValueError, match="device memory"):
+        p.forward_stats(*good[:3])
+    with pytest.raises(TypeError):
+        p.forward_attend(np.zeros((H, Lq, d)), *good[1:])
