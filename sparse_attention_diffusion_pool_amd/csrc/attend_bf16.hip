@@ -17,16 +17,15 @@
 // Keys stream in steps of 64 through two LDS stages (K and V halves, 16 KB each): step s + 1 is
 // copied global -> LDS (buffer loads, rows past the block end read as zero) while step s is
 // computed. A key block of 128 rows takes two steps; the selected block list is staged in LDS.
-// Softmax runs in the log2 domain: Q is pre-scaled by scale * log2 e, and each score tile starts
-// from one MFMA that adds -m (the row's reference, exact in bf16), so the accumulators hold the
-// exponent arguments. The reference and the accumulators are rescaled only when a row's max grows
-// by more than 2^8 (exact: numerator and denominator share the stale reference, and p <= 256
-// stays far inside fp32/bf16 range).
-// Phase 2: pooled tokens (kbar_j, vbar_j) through the same steps; each token's bias (log2 n_j, or
-// -inf outside U_i, from the bit mask in LDS, or past N_b) enters through the shift MFMA, so the
-// softmax is the exact steps' own. beta (the sum of p / n_j) takes each pooled step's row sum over
-// B, plus a correction for a ragged last block's token. Phase 3: O += (beta * scale) (q H-bar),
-// from the pre-scaled q.
+// Softmax runs in the log2 domain: Q enters the MFMA as given, and one FMA per score turns the raw
+// q.k into the exponent argument scale log2(e) q.k - m (m = the row's reference). The reference is
+// moved only when a row's max grows by more than 2^8 (exact: numerator and denominator share the
+// stale reference, and p <= 256 stays far inside fp32/bf16 range).
+// Phase 2: pooled tokens (kbar_j, vbar_j) through the same steps; each token's bias (ln n_j, or
+// -inf outside U_i, from the bit mask in LDS, or past N_b) enters through one MFMA that starts the
+// score tile, so the softmax is the exact steps' own. beta (the sum of p / n_j) takes each pooled
+// step's row sum over B, plus a correction for a ragged last block's token. Phase 3:
+// O += (beta * scale) (q H-bar).
 // Epilogue: out = O / l, rounded to bf16, staged through LDS for 16-byte row stores.
 #include "dev_common.h"
 #include "pisa_internal.h"
@@ -36,14 +35,6 @@ namespace {
 
 constexpr int kMaskWords = (8192 + 128) / 32;  // N_b <= 8192, rounded up to a tile
 constexpr float kLazy = 8.0f;                   // rescale threshold (log2 units)
-
-// x rounded to a bf16 value >= x (finite x): the softmax reference must be exact in bf16 (it enters
-// an MFMA operand) and must not fall below the running max (p <= 2^kLazy).
-__device__ __forceinline__ float bf16_ceil(float x) {
-  uint32_t u = __float_as_uint(x);
-  u = (x > 0.0f) ? ((u + 0xffffu) & 0xffff0000u) : (u & 0xffff0000u);
-  return __uint_as_float(u);
-}
 
 // Per-lane LDS read offsets, computed once (relative to a tile's first row r0, r0 % 16 == 0):
 //   krd[s]: 16-byte row read of row r0 + l32, d-chunk 2 s + hh (row-read swizzle)
@@ -245,23 +236,20 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
     for (int s = 0; s < 8; ++s)
       qreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, row * 256 + (16 * s + 8 * hh) * 2));
   }
-  // Q pre-scaled by scale * log2 e (rounded to bf16): the MFMA then gives scores in log2 units
+  // Q stays as given (exact bf16): the MFMA gives raw q.k in fp32, and the softmax scale (times
+  // log2 e) is applied in fp32 by one FMA per score, x = cs q.k - m. Rounding cs q to bf16 instead
+  // would add an error of up to 2^-9 |cs q.k| to every exponent, which sharp score distributions
+  // (spreads of 6 and more) turn into output errors above the bf16 tolerance.
   const float cs = dm.scale * kLog2e;
-#pragma unroll
-  for (int s = 0; s < 8; ++s)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qreg[s][e] = (__bf16)((float)qreg[s][e] * cs);
-  // Operands of the shift MFMA that starts every score tile, D[key][q] = sum over k < 3 of
-  // A[key][k] B[k][q]: B row 0 holds -m of the lane's query (0 while m = -inf; it changes only with
-  // m), rows 1 and 2 hold 1. A column 0 is 1; columns 1 and 2 are the key's bias: 0 for exact keys;
-  // for a pooled token log2 n_j, or -inf for a selected block or j >= N_b. log2 B is exact in bf16;
-  // the ragged last block's log2 n_last is split into a bf16 head (column 1) and tail (column 2).
-  bf16x8 shift_a = {}, shift_b = {};
-  shift_a[0] = (__bf16)(hh == 0 ? 1.0f : 0.0f);
+  // Operands of the bias MFMA that starts every pooled score tile, D[key][q] = sum over k < 3 of
+  // A[key][k] B[k][q] with B rows 1 and 2 = 1: A columns 1 and 2 hold the token's bias in raw score
+  // units, log2(n_j) / cs split into a bf16 head and tail, or -inf for a selected block or j >= N_b.
+  bf16x8 shift_b = {};
   shift_b[1] = (__bf16)(hh == 0 ? 1.0f : 0.0f);
   shift_b[2] = shift_b[1];
-  const float lgB = __log2f((float)B), lgLast = __log2f((float)dm.n_last);
-  const __bf16 lgLast_hi = (__bf16)lgLast, lgLast_lo = (__bf16)(lgLast - (float)lgLast_hi);
+  const float bB = __log2f((float)B) / cs, bLast = __log2f((float)dm.n_last) / cs;
+  const __bf16 bB_hi = (__bf16)bB, bB_lo = (__bf16)(bB - (float)bB_hi);
+  const __bf16 bLast_hi = (__bf16)bLast, bLast_lo = (__bf16)(bLast - (float)bLast_hi);
   const float invB = 1.0f / (float)B;
   // beta takes a pooled step's row sum over B. For a ragged last block (n_last < B) the step that
   // holds its token (s_last) adds p (1 / n_last - 1 / B), with p read from the token's accumulator:
@@ -271,7 +259,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
   const int r_last = (Nb - 1) % kKT, i_last = r_last % 32;
   const int u_last = r_last / 32, hh_last = (i_last / 4) % 2, x_last = (i_last % 4) + 4 * (i_last / 8);
   const float corr_last = 1.0f / (float)dm.n_last - invB;
-  float m = -INFINITY, lsum = 0.f, beta = 0.f;
+  // m: the row's softmax reference (log2 units); neg_m = -m, or 0 while m = -inf (every key seen
+  // so far masked)
+  float m = -INFINITY, neg_m = 0.f, lsum = 0.f, beta = 0.f;
   f32x16 O[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) O[dt] = f32x16{};
@@ -290,9 +280,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
     if (s + 1 < S_all) issue(s + 1, Stage<ST ^ 1>{});
     f32x16 Sc[NT];
     bf16x8 P[NT][2];
-    // The accumulators start at -m (m is exact in bf16), so the MFMA returns the exponent argument
-    // cs q.k - m and the softmax needs no FMA per score. (A lane whose keys have all been masked so
-    // far still has m = -inf: its shift is 0.)
+    // Exact tiles start from zero; pooled tiles from the bias MFMA. After the products, one FMA per
+    // score gives the exponent argument x = cs (q.k + bias) - m.
     if constexpr (KIND == 2) {
       // A row = key l32 of subtile t: pooled token j = (s - E) kKT + 32 t + l32
       const int key_base = (s - E) * kKT;
@@ -301,16 +290,20 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
         const int j = key_base + 32 * t + (int)l32;
         const bool sel_j = (selm[(key_base + 32 * t) / 32] >> l32) & 1u;
         const bool ok = j < Nb && !sel_j && hh == 0;
-        bf16x8 a = shift_a;
-        a[1] = ok ? (j == Nb - 1 ? lgLast_hi : (__bf16)lgB) : (__bf16)(hh == 0 ? -INFINITY : 0.0f);
-        a[2] = ok && j == Nb - 1 ? lgLast_lo : (__bf16)0.0f;
+        const bool last = j == Nb - 1;
+        bf16x8 a = {};
+        a[1] = ok ? (last ? bLast_hi : bB_hi) : (__bf16)(hh == 0 ? -INFINITY : 0.0f);
+        a[2] = ok ? (last ? bLast_lo : bB_lo) : (__bf16)0.0f;
         Sc[t] = mfma32(a, shift_b, f32x16{});
       }
+      qk_tile<NT, true>(ST ? sK1 : sK0, 0, qreg, Sc, lofs);
     } else {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) Sc[t] = mfma32(shift_a, shift_b, f32x16{});
+      qk_tile<NT, false>(ST ? sK1 : sK0, 0, qreg, Sc, lofs);
     }
-    qk_tile<NT, true>(ST ? sK1 : sK0, 0, qreg, Sc, lofs);
+#pragma unroll
+    for (int u = 0; u < NT; ++u)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) Sc[u][x] = fmaf(Sc[u][x], cs, neg_m);
     float mx = -INFINITY;  // of the scores relative to mref
     if constexpr (KIND == 1) {
       const int valid = rows_last - kKT * ((E - 1) % SPB);  // rows of the partial step
@@ -330,11 +323,11 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
     const bool up = mx > (m == -INFINITY ? -INFINITY : kLazy);
     if (__builtin_expect(__ballot(up) != 0, 0)) {
       const float mref = m == -INFINITY ? 0.0f : m;
-      const float m_new = up ? bf16_ceil(mref + mx) : m;
+      const float m_new = up ? mref + mx : m;
       const float alpha = up ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;
       const float shift = up ? m_new - mref : 0.0f;
       m = m_new;
-      shift_b[0] = (__bf16)(hh == 0 && m != -INFINITY ? -m : 0.0f);
+      neg_m = m == -INFINITY ? 0.0f : -m;
       lsum *= alpha;
       beta *= alpha;
 #pragma unroll
@@ -410,7 +403,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
   // ---- phase 3: global first-order correction --------------------------------------------
   if (do_first) {
     f32x16 T2[2];
-    const float bt = beta * (dm.scale / cs);  // q is pre-scaled by cs
+    const float bt = beta * dm.scale;
     qk_tile<2>(hstage ? sK1 : sK0, 0, qreg, T2, lofs);  // H-bar^T rows 0..63
     O[0] += bt * T2[0];
     O[1] += bt * T2[1];

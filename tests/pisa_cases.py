@@ -151,6 +151,26 @@ def check_stats(res, h: int, ref):
         assert err_m < 2e-5, f"M: rel err {err_m}"
 
 
+def check_every_head(res, heads=None, workers: int = 8, label: str = ""):
+    """Statistics (if copied) and selection of every head against the oracle, in a thread pool
+    (NumPy releases the GIL in its kernels). Logs and returns the near-tie row count per head."""
+    import concurrent.futures as cf
+
+    heads = list(range(res["out"].shape[0])) if heads is None else list(heads)
+
+    def one(h):
+        ref, _, nsel = oracle_head(res, h, query_blocks=[])
+        if "stats" in res:
+            check_stats(res, h, ref)
+        return h, nsel
+
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        ties = dict(ex.map(one, heads))
+    log(f"[parity] {label}: statistics and selection of {len(heads)} heads match; near-tie rows per "
+        f"head: {[ties[h] for h in heads]}")
+    return ties
+
+
 def sample_blocks(nb: int, n: int, seed: int):
     rng = np.random.default_rng(seed)
     pick = set(rng.choice(nb, size=min(n, nb), replace=False).tolist())

@@ -9,8 +9,8 @@ import numpy as np
 import pytest
 import torch
 
-from pisa_cases import (assert_close, check_stats, compare_rows, gpu_run, log, oracle_head,
-                        sample_blocks)
+from pisa_cases import (assert_close, check_every_head, check_stats, compare_rows, gpu_run, log,
+                        oracle_head, sample_blocks)
 from workloads import custom, layer_inputs, workload
 
 pytestmark = pytest.mark.gpu
@@ -162,17 +162,14 @@ def test_spectral_wan720p_selection():
 def test_flux_like_layer():
     w = workload("flux-like-L4608")
     res = gpu_run(w, want_stats=True)
-    H = w.H
-    for h in range(H):
-        if h in (0, 7, 15, 23):
-            continue
-        oracle_head(res, h, query_blocks=[])  # selection check only
-    _full_check(res, heads=[0, 7, 15, 23], label=w.name)
+    check_every_head(res, label=w.name)
+    _full_check(res, heads=[0, 7, 15, 23], label=w.name, stats=False)
 
 
 # ---------------------------------------------------------------------------------------------
-# Full-size video layers, in the launch configuration the benchmark times: three heads' complete
-# selection and statistics, outputs on sampled query blocks (first, last/ragged, random).
+# Full-size video layers, in the launch configuration the benchmark times: every head's complete
+# statistics and selection; outputs on sampled query blocks (first, last/ragged, random) of three
+# heads, and at Wan-720p every query block of the first and last head.
 # ---------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name", ["wan480p-like-L32760", "wan720p-like-L75600", "hunyuan720p-like-L119056"])
@@ -180,9 +177,13 @@ def test_full_size_layers(name):
     w = workload(name)
     res = gpu_run(w, want_stats=True)
     nb = res["info"]["n_blocks"]
+    check_every_head(res, label=w.name)
     heads = [0, w.H // 2, w.H - 1]
     qb = sample_blocks(nb, 10, seed=w.cfg_id)
-    _full_check(res, heads=heads, label=w.name, query_blocks=qb)
+    _full_check(res, heads=heads, label=w.name, query_blocks=qb, stats=False)
+    if name == "wan720p-like-L75600":
+        _full_check(res, heads=[0, w.H - 1], label=f"{w.name} every query block of heads 0, {w.H - 1}",
+                    stats=False)
 
 
 # ---------------------------------------------------------------------------------------------
