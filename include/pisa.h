@@ -143,6 +143,19 @@ pisa_status pisa_plan_attach_workspace(pisa_plan_t *plan, void *dev_ptr, size_t 
 pisa_status pisa_forward(pisa_plan_t *plan, const void *Q, const void *K, const void *V, void *out,
                          hipStream_t stream);
 
+/* pisa_forward without an attached workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). The
+ * statistics, selection and H-bar live in a static device array of 160 MiB per GPU (allocated
+ * when the library's code is loaded, held until the process ends), which covers plans whose
+ * workspace_bytes is at most 160 MiB (every bundled workload: the Wan2.1-14B-like 720p layer needs
+ * 149 MiB); a larger plan gives PISA_ERR_WORKSPACE. The call allocates nothing and needs no
+ * attached workspace (one attached to the plan is ignored). Every call on a GPU shares that GPU's
+ * array and leaves its contents behind (every part is written before it is read, so nothing needs
+ * clearing): calls that can overlap on one GPU (two streams, two threads) race and must be
+ * serialised by the caller. Same arguments, checks and results as pisa_forward. */
+pisa_status pisa_forward_noalloc(pisa_plan_t *plan, const void *Q, const void *K, const void *V, void *out,
+                                 hipStream_t stream);
+
 /* Stage 1: block statistics into the workspace (centroids, value sums, pooled queries, H-bar,
  * M_j). Reads Q, K, V. */
 pisa_status pisa_forward_stats(pisa_plan_t *plan, const void *Q, const void *K, const void *V,

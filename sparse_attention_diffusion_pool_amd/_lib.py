@@ -50,6 +50,7 @@ _SIGS = {
     "pisa_plan_info": (ctypes.c_int, [_P, ctypes.POINTER(PlanInfo)]),
     "pisa_plan_attach_workspace": (ctypes.c_int, [_P, _P, ctypes.c_size_t]),
     "pisa_forward": (ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
+    "pisa_forward_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
     "pisa_forward_stats": (ctypes.c_int, [_P, _P, _P, _P, _P]),
     "pisa_forward_route": (ctypes.c_int, [_P, _P]),
     "pisa_forward_attend": (ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
@@ -187,6 +188,12 @@ class Plan:
     def forward(self, Q, K, V, out, stream=None):
         q, k, v, o = self._args(Q=Q, K=K, V=V, out=out)
         check(load().pisa_forward(self._h, q, k, v, o, _stream(stream)), "pisa_forward")
+        return out
+
+    def forward_noalloc(self, Q, K, V, out, stream=None):
+        """pisa_forward_noalloc: the forward pass on the library's static per-GPU workspace."""
+        q, k, v, o = self._args(Q=Q, K=K, V=V, out=out)
+        check(load().pisa_forward_noalloc(self._h, q, k, v, o, _stream(stream)), "pisa_forward_noalloc")
         return out
 
     def forward_stats(self, Q, K, V, stream=None):

@@ -449,6 +449,25 @@ pisa_status pisa_forward(pisa_plan_t* p, const void* Q, const void* K, const voi
   return run_forward(p, p->ws, Q, K, V, out, stream);
 }
 
+pisa_status pisa_forward_noalloc(pisa_plan_t* p, const void* Q, const void* K, const void* V, void* out,
+                                 hipStream_t stream) {
+  if (!valid_plan(p)) return fail(PISA_ERR_INVALID_HANDLE, "invalid or destroyed plan");
+  pisa_status s = check_supported(p->dm);
+  if (s != PISA_OK) return s;
+  const size_t need = pisa::workspace_layout(p->dm).total;
+  if (need > pisa::kStaticWorkspaceBytes)
+    return fail(PISA_ERR_WORKSPACE, "the plan needs %zu bytes of workspace; the static workspace holds %zu",
+                need, pisa::kStaticWorkspaceBytes);
+  if (out == nullptr) return fail(PISA_ERR_INVALID_ARGUMENT, "out is NULL");
+  if ((s = check_tensors(p, Q, K, V, out)) != PISA_OK) return s;
+  if ((s = check_device()) != PISA_OK) return s;
+  if ((s = check_inputs_resident(p, Q, K, V, out)) != PISA_OK) return s;
+  void* ws = nullptr;
+  hipError_t e = pisa::static_workspace(stream, &ws);
+  if (e != hipSuccess) return fail(PISA_ERR_DEVICE, "static workspace lookup: %s", hipGetErrorString(e));
+  return run_forward(p, ws, Q, K, V, out, stream);
+}
+
 pisa_status pisa_plan_destroy(pisa_plan_t* p) {
   {
     std::lock_guard<std::mutex> g(g_plans_mu);

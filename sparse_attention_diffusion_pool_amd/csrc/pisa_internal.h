@@ -57,6 +57,13 @@ struct Layout {
 };
 
 Layout workspace_layout(const Dims& dm);
+
+// Size of the static workspace of pisa_forward_noalloc (a file-scope device array per GPU): the
+// plans of every bundled workload fit (the Wan2.1-14B-like 720p layer needs 149 MiB).
+constexpr size_t kStaticWorkspaceBytes = size_t(160) << 20;
+
+// Device address of that array on the stream's device (looked up once per device, then cached).
+hipError_t static_workspace(hipStream_t stream, void** ptr);
 Work workspace_pointers(const Dims& dm, void* base);
 
 // Statistics (precompute), routing and the fused attention kernel launchers. Each returns the
