@@ -35,6 +35,8 @@ namespace {
 
 constexpr int kMaskWords = (8192 + 128) / 32;  // N_b <= 8192, rounded up to a tile
 constexpr float kLazy = 8.0f;                   // rescale threshold (log2 units)
+constexpr float kSumHi = 4294967296.0f;         // 2^32: a step's row sum above this moves the reference
+constexpr float kSumLo = 2.3283064365386963e-10f;  // 2^-32: ... or below this while nothing is summed
 
 // Per-lane LDS read offsets, computed once (relative to a tile's first row r0, r0 % 16 == 0):
 //   krd[s]: 16-byte row read of row r0 + l32, d-chunk 2 s + hh (row-read swizzle)
@@ -45,16 +47,18 @@ struct LaneOffsets {
   uint32_t vrd[4];
 };
 
-__device__ __forceinline__ LaneOffsets lane_offsets(uint32_t lane) {
+// base: byte offset of the wave's first key row in a tile (a multiple of 16 rows: the swizzles
+// only depend on the row modulo 16)
+__device__ __forceinline__ LaneOffsets lane_offsets(uint32_t lane, uint32_t base = 0) {
   const uint32_t hh = lane >> 5, l32 = lane & 31, g16 = (lane >> 4) & 1, l16 = lane & 15;
   LaneOffsets o;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) o.krd[s] = l32 * 256 + swz_row(l32, 2 * s + hh) * 16;
+  for (int s = 0; s < 8; ++s) o.krd[s] = base + l32 * 256 + swz_row(l32, 2 * s + hh) * 16;
   const uint32_t dr = l16 >> 2;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
     const uint32_t byte = (32 * dt + 16 * g16 + 4 * (l16 & 3)) * 2;
-    o.vrd[dt] = (4 * hh + dr) * 256 + swz_tr(dr, byte >> 4) * 16 + (byte & 15);
+    o.vrd[dt] = base + (4 * hh + dr) * 256 + swz_tr(dr, byte >> 4) * 16 + (byte & 15);
   }
   return o;
 }
@@ -142,14 +146,16 @@ constexpr int kKT = 64;           // keys per step
 constexpr int kIdxLds = 4096;     // selected-block list entries staged in LDS
 
 template <int BLK>
-__global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const __bf16* __restrict__ Q,
-                                                          const __bf16* __restrict__ K,
-                                                          const __bf16* __restrict__ V,
-                                                          __bf16* __restrict__ out) {
-  constexpr int NW = BLK / 32;     // waves = query groups
+__global__ __launch_bounds__(256, 2) void attend_bf16(Dims dm, Work w, const __bf16* __restrict__ Q,
+                                                      const __bf16* __restrict__ K,
+                                                      const __bf16* __restrict__ V,
+                                                      __bf16* __restrict__ out) {
+  constexpr int NW = 4;            // waves
+  constexpr int KS = 128 / BLK;    // waves per query group: each takes 1/KS of every step's keys
+  constexpr int QG = NW / KS;      // query groups of 32 rows
   constexpr int NTH = 64 * NW;
   constexpr int SPB = BLK / kKT;   // steps per key block (and per pooled tile)
-  constexpr int NT = kKT / 32;     // 32-key subtiles per step
+  constexpr int NT = kKT / 32 / KS;  // 32-key subtiles per wave and step
   constexpr int TB = kKT * 256;    // bytes of one K (or V) half
   // Two stages (K and V halves) as four distinct LDS objects: the compiler then sees that reading
   // one stage does not depend on the direct-to-LDS copies into the other.
@@ -161,9 +167,14 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
   __shared__ uint16_t sidx[kIdxLds];
 
   const int item = item_of(blockIdx.x, gridDim.x);
-  const int h = item / dm.Nb, i = item % dm.Nb;
+  // (the divisions run on the vector unit: readfirstlane keeps the results, and every address
+  // derived from them, in scalar registers)
+  const int h = __builtin_amdgcn_readfirstlane(item / dm.Nb), i = __builtin_amdgcn_readfirstlane(item % dm.Nb);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS bases stay scalar
+  // query group qg (rows 32 qg ..), key part kh: with B = 64 a query group is two waves, each
+  // running its own online softmax over one half of every step's keys, merged at the end
+  const int qg = KS == 1 ? wave : wave % QG, kh = KS == 1 ? 0 : wave / QG;
   const uint32_t hh = lane >> 5, l32 = lane & 31;
   const int Nb = dm.Nb, B = dm.B, kk = dm.k;
   const int n_i = (i == Nb - 1) ? dm.n_last : B;
@@ -214,24 +225,24 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
       const int n_j = (j == Nb - 1) ? dm.n_last : B;
       const uint32_t off = ((uint32_t)j * (uint32_t)B + (uint32_t)r0) * 256u;
       const uint32_t bytes = (uint32_t)(n_j - r0) * 256;  // rows past the block end read as zero
-      copy_tile_chunks<kKT, NW, false>(rsrc_words(Kh + off, bytes), Ks, cl_row, wave);
-      copy_tile_chunks<kKT, NW, true>(rsrc_words(Vh + off, bytes), Vs, cl_tr, wave);
+      copy_tile_chunks<kKT, NW, false>(Kh + off, bytes, Ks, cl_row, wave);
+      copy_tile_chunks<kKT, NW, true>(Vh + off, bytes, Vs, cl_tr, wave);
     } else if (s < S_main) {
       const size_t g0 = (size_t)(s - E) * kKT * 128;
-      copy_tile_chunks<kKT, NW, false>(rsrc_words(kl + g0, kKT * 256), Ks, cl_row, wave);
-      copy_tile_chunks<kKT, NW, true>(rsrc_words(vl + g0, kKT * 256), Vs, cl_tr, wave);
+      copy_tile_chunks<kKT, NW, false>(kl + g0, kKT * 256, Ks, cl_row, wave);
+      copy_tile_chunks<kKT, NW, true>(vl + g0, kKT * 256, Vs, cl_tr, wave);
     } else {
-      copy_tile_chunks<kKT, NW, false>(rsrc_words(ht, kKT * 256), Ks, cl_row, wave);
-      copy_tile_chunks<kKT, NW, false>(rsrc_words(ht + kKT * 128, kKT * 256), Vs, cl_row, wave);
+      copy_tile_chunks<kKT, NW, false>(ht, kKT * 256, Ks, cl_row, wave);
+      copy_tile_chunks<kKT, NW, false>(ht + kKT * 128, kKT * 256, Vs, cl_row, wave);
     }
   };
   issue(0, Stage<0>{});
 
-  // Q^T operand: query row 32 wave + l32 of the block, d = 16 s + 8 hh .. +7
+  // Q^T operand: query row 32 qg + l32 of the block, d = 16 s + 8 hh .. +7
   bf16x8 qreg[8];
   {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head + (size_t)i * B * 128, n_i * 256);
-    const uint32_t row = 32 * wave + l32;
+    const uint32_t row = 32 * qg + l32;
 #pragma unroll
     for (int s = 0; s < 8; ++s)
       qreg[s] = __builtin_bit_cast(bf16x8, buf_load16(rq, row * 256 + (16 * s + 8 * hh) * 2));
@@ -241,6 +252,24 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
   // would add an error of up to 2^-9 |cs q.k| to every exponent, which sharp score distributions
   // (spreads of 6 and more) turn into output errors above the bf16 tolerance.
   const float cs = dm.scale * kLog2e;
+  // The pooled centroids are stored relative to the head's key centre c: their scores get
+  // cs q.c back through the FMA's addend (q.c in fp32, over the lane's half of d, then the pair).
+  float csqc = 0.f;
+  if (nc > 0) {
+    const float* kcen = w.kc + (size_t)h * 128;
+    float a = 0.f;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const f32x4 c0 = *reinterpret_cast<const f32x4*>(kcen + 16 * s + 8 * hh);
+      const f32x4 c1 = *reinterpret_cast<const f32x4*>(kcen + 16 * s + 8 * hh + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a = fmaf((float)qreg[s][e], c0[e], a);
+        a = fmaf((float)qreg[s][e + 4], c1[e], a);
+      }
+    }
+    csqc = cs * (a + __shfl_xor(a, 32));
+  }
   // Operands of the bias MFMA that starts every pooled score tile, D[key][q] = sum over k < 3 of
   // A[key][k] B[k][q] with B rows 1 and 2 = 1: A columns 1 and 2 hold the token's bias in raw score
   // units, log2(n_j) / cs split into a bf16 head and tail, or -inf for a selected block or j >= N_b.
@@ -259,19 +288,23 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
   const int r_last = (Nb - 1) % kKT, i_last = r_last % 32;
   const int u_last = r_last / 32, hh_last = (i_last / 4) % 2, x_last = (i_last % 4) + 4 * (i_last / 8);
   const float corr_last = 1.0f / (float)dm.n_last - invB;
-  // m: the row's softmax reference (log2 units); neg_m = -m, or 0 while m = -inf (every key seen
-  // so far masked)
-  float m = -INFINITY, neg_m = 0.f, lsum = 0.f, beta = 0.f;
+  // m: the row's softmax reference (log2 units), 0 until a step moves it; neg_m = -m
+  float m = 0.f, neg_m = 0.f, lsum = 0.f, beta = 0.f;
   f32x16 O[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) O[dt] = f32x16{};
-  const LaneOffsets lofs = lane_offsets(lane);
+  const LaneOffsets lofs = lane_offsets(lane, (uint32_t)(32 * NT * kh) * 256u);
   // The two waves sharing a SIMD come from different workgroups. A fixed priority order between
   // them (by the parity of the hardware wave slot, HW_ID bits 0..3) lets one run at its own pace
   // while the other fills its gaps, instead of both competing for every issue slot.
   if (__builtin_amdgcn_s_getreg((4 << 0) | (0 << 6) | (3 << 11)) & 1) __builtin_amdgcn_s_setprio(2);
 
   // One step s (ST = s & 1). KIND 0 = exact, 1 = exact partial (masked past valid rows), 2 = pooled.
+  // The reference m is not moved step by step: the probabilities are formed against it as it
+  // stands, and only a step whose row sum leaves [2^-32 (while nothing has been summed), 2^32]
+  // (or is not finite) takes the rare path that recomputes the step's scores and moves m to the
+  // row's maximum. Every probability then stays below 2^32 (far inside fp32 and bf16 range), and
+  // numerator and denominator always share the reference.
   auto step = [&](int s, auto stc, auto kc) {
     constexpr int ST = decltype(stc)::value;
     constexpr int KIND = decltype(kc)::value;
@@ -280,97 +313,107 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
     if (s + 1 < S_all) issue(s + 1, Stage<ST ^ 1>{});
     f32x16 Sc[NT];
     bf16x8 P[NT][2];
+    float s_tok = -INFINITY;
     // Exact tiles start from zero; pooled tiles from the bias MFMA. After the products, one FMA per
-    // score gives the exponent argument x = cs (q.k + bias) - m.
-    if constexpr (KIND == 2) {
-      // A row = key l32 of subtile t: pooled token j = (s - E) kKT + 32 t + l32
-      const int key_base = (s - E) * kKT;
+    // score gives the exponent argument x = cs (q.k + bias) - m (pooled: q.(kbar_j - c) + cs q.c).
+    auto scores = [&]() __attribute__((always_inline)) {
+      if constexpr (KIND == 2) {
+        // A row = key l32 of subtile t: pooled token j = (s - E) kKT + 32 (NT kh + t) + l32
+        const int key_base = (s - E) * kKT + 32 * NT * kh;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int j = key_base + 32 * t + (int)l32;
-        const bool sel_j = (selm[(key_base + 32 * t) / 32] >> l32) & 1u;
-        const bool ok = j < Nb && !sel_j && hh == 0;
-        const bool last = j == Nb - 1;
-        bf16x8 a = {};
-        a[1] = ok ? (last ? bLast_hi : bB_hi) : (__bf16)(hh == 0 ? -INFINITY : 0.0f);
-        a[2] = ok ? (last ? bLast_lo : bB_lo) : (__bf16)0.0f;
-        Sc[t] = mfma32(a, shift_b, f32x16{});
+        for (int t = 0; t < NT; ++t) {
+          const int j = key_base + 32 * t + (int)l32;
+          const bool sel_j = (selm[(key_base + 32 * t) / 32] >> l32) & 1u;
+          const bool ok = j < Nb && !sel_j && hh == 0;
+          const bool last = j == Nb - 1;
+          bf16x8 a = {};
+          a[1] = ok ? (last ? bLast_hi : bB_hi) : (__bf16)(hh == 0 ? -INFINITY : 0.0f);
+          a[2] = ok ? (last ? bLast_lo : bB_lo) : (__bf16)0.0f;
+          Sc[t] = mfma32(a, shift_b, f32x16{});
+        }
+        qk_tile<NT, true>(ST ? sK1 : sK0, 0, qreg, Sc, lofs);
+      } else {
+        qk_tile<NT, false>(ST ? sK1 : sK0, 0, qreg, Sc, lofs);
       }
-      qk_tile<NT, true>(ST ? sK1 : sK0, 0, qreg, Sc, lofs);
-    } else {
-      qk_tile<NT, false>(ST ? sK1 : sK0, 0, qreg, Sc, lofs);
-    }
-#pragma unroll
-    for (int u = 0; u < NT; ++u)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) Sc[u][x] = fmaf(Sc[u][x], cs, neg_m);
-    float mx = -INFINITY;  // of the scores relative to mref
-    if constexpr (KIND == 1) {
-      const int valid = rows_last - kKT * ((E - 1) % SPB);  // rows of the partial step
+      const float add = KIND == 2 ? neg_m + csqc : neg_m;
 #pragma unroll
       for (int u = 0; u < NT; ++u)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          const int key = 32 * u + 8 * (x >> 2) + 4 * hh + (x & 3);
-          if (key >= valid) Sc[u][x] = -INFINITY;
-        }
-    }
+        for (int x = 0; x < 16; ++x) Sc[u][x] = fmaf(Sc[u][x], cs, add);
+      if constexpr (KIND == 1) {
+        // key 32 u + 8 (x / 4) + 4 hh + x % 4 of this lane is masked when it reaches the step's
+        // valid rows; comparing the constant part with (valid - 4 hh) keeps the key indices out of
+        // registers
+        const int vrel = rows_last - kKT * ((E - 1) % SPB) - 32 * NT * kh - 4 * (int)hh;
 #pragma unroll
-    for (int u = 0; u < NT; ++u)
+        for (int u = 0; u < NT; ++u)
 #pragma unroll
-      for (int x = 0; x < 16; ++x) mx = fmaxf(mx, Sc[u][x]);
-    mx = xor32_max(mx);
-    const bool up = mx > (m == -INFINITY ? -INFINITY : kLazy);
-    if (__builtin_expect(__ballot(up) != 0, 0)) {
-      const float mref = m == -INFINITY ? 0.0f : m;
-      const float m_new = up ? mref + mx : m;
-      const float alpha = up ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;
-      const float shift = up ? m_new - mref : 0.0f;
-      m = m_new;
-      neg_m = m == -INFINITY ? 0.0f : -m;
-      lsum *= alpha;
-      beta *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) O[dt] *= alpha;
-#pragma unroll
-      for (int u = 0; u < NT; ++u) Sc[u] -= shift;
-    }
-    // score of the ragged last block's token in its step (wave-uniform branch), taken before the
-    // exponentials so that the score registers need not outlive them
-    float s_tok = -INFINITY;
-    if constexpr (KIND == 2) {
-      if (s == s_last) {
-        s_tok = Sc[0][x_last];
-#pragma unroll
-        for (int u = 1; u < NT; ++u)
-          if (u == u_last) s_tok = Sc[u][x_last];
+          for (int x = 0; x < 16; ++x)
+            if (32 * u + 8 * (x >> 2) + (x & 3) >= vrel) Sc[u][x] = -INFINITY;
       }
-    }
+    };
+    // probabilities (rounded to bf16: the values the numerator's MFMA uses) and their sum over the
+    // lane's keys, in four independent dot2 chains; the ragged last block's pooled token score is
+    // taken first (wave-uniform branch)
+    auto probs = [&]() __attribute__((always_inline)) {
+      if constexpr (KIND == 2) {
+        if (s == s_last && u_last / NT == kh) {
+          s_tok = Sc[0][x_last];
 #pragma unroll
-    for (int u = 0; u < NT; ++u)
+          for (int u = 1; u < NT; ++u)
+            if (u == u_last % NT) s_tok = Sc[u][x_last];
+        }
+      }
 #pragma unroll
-      for (int v = 0; v < 2; ++v)
+      for (int u = 0; u < NT; ++u)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) P[u][v][e] = (__bf16)__builtin_amdgcn_exp2f(Sc[u][8 * v + e]);
-    {
-      // row sum of the rounded probabilities (those the numerator's MFMA uses), two per dot2;
-      // a pooled step's sum, divided by the block size, also feeds beta
+        for (int v = 0; v < 2; ++v)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) P[u][v][e] = (__bf16)__builtin_amdgcn_exp2f(Sc[u][8 * v + e]);
       const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-      float ps = KIND == 2 ? 0.0f : lsum;
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int u = 0; u < NT; ++u)
 #pragma unroll
         for (int v = 0; v < 2; ++v)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            ps = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P[u][v][2 * e], P[u][v][2 * e + 1]}, ones, ps, false);
-      if constexpr (KIND == 2) {
-        lsum += ps;
-        beta = fmaf(ps, invB, beta);
-        if (s == s_last && (int)hh == hh_last) beta = fmaf(__builtin_amdgcn_exp2f(s_tok), corr_last, beta);
-      } else {
-        lsum = ps;
-      }
+            part[e] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{P[u][v][2 * e], P[u][v][2 * e + 1]}, ones, part[e],
+                                                      false);
+      return (part[0] + part[1]) + (part[2] + part[3]);
+    };
+    scores();
+    float ps = probs();
+    const bool bad = !(ps <= kSumHi) || (lsum == 0.0f && ps < kSumLo);
+    if (__builtin_expect(__ballot(bad) != 0, 0)) {
+      // rare: the step's scores again (the tile is still in LDS), and the reference of every row
+      // whose maximum is above 2^8 or that has nothing summed yet moves to that maximum
+      scores();
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < NT; ++u)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) mx = fmaxf(mx, Sc[u][x]);
+      mx = xor32_max(mx);
+      const float lrow = lsum + __shfl_xor(lsum, 32);
+      const bool up = mx > -INFINITY && (mx > kLazy || lrow == 0.0f);
+      const float shift = up ? mx : 0.0f;
+      const float alpha = __builtin_amdgcn_exp2f(-shift);
+      m += shift;
+      neg_m = -m;
+      lsum *= alpha;
+      beta *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) O[dt] *= alpha;
+#pragma unroll
+      for (int u = 0; u < NT; ++u) Sc[u] -= shift;
+      ps = probs();
+    }
+    lsum += ps;
+    if constexpr (KIND == 2) {
+      // a pooled step's sum, divided by the block size, also feeds beta
+      beta = fmaf(ps, invB, beta);
+      if (s == s_last && (int)hh == hh_last) beta = fmaf(__builtin_amdgcn_exp2f(s_tok), corr_last, beta);
     }
     pv_tile<NT>(ST ? sV1 : sV0, 0, P, O, lofs);
   };
@@ -400,8 +443,40 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
   wait_vmem();
   __syncthreads();  // every wave done with the last step; the H-bar^T tile (if any) has landed
   const int hstage = S_main & 1;
+  const int xs = do_first ? (hstage ^ 1) : 0;  // the stage free for exchanges and output staging
+  if constexpr (KS == 2) {
+    // merge the two key halves of each query group: the kh = 1 wave hands its reference,
+    // denominator, beta and numerator to the kh = 0 wave through LDS (numerators in the free
+    // stage, one array per group; the scalars in the selection list's space, no longer read)
+    float* xo = reinterpret_cast<float*>(qg == 0 ? (xs ? sK1 : sK0) : (xs ? sV1 : sV0));
+    float* xm = reinterpret_cast<float*>(sidx) + qg * 3 * 64;
+    if (kh == 1) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) xo[(dt * 16 + x) * 64 + lane] = O[dt][x];
+      xm[lane] = m;
+      xm[64 + lane] = lsum;
+      xm[128 + lane] = beta;
+    }
+    __syncthreads();
+    if (kh == 0) {
+      const float mp = xm[lane], lp = xm[64 + lane], bp = xm[128 + lane];
+      const float mm = fmaxf(m, mp);
+      const float a0 = __builtin_amdgcn_exp2f(m - mm), a1 = __builtin_amdgcn_exp2f(mp - mm);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) O[dt][x] = fmaf(a1, xo[(dt * 16 + x) * 64 + lane], a0 * O[dt][x]);
+      m = mm;
+      lsum = fmaf(a1, lp, a0 * lsum);
+      beta = fmaf(a1, bp, a0 * beta);
+    }
+    __syncthreads();  // the exchange is read before the stage is reused for the output rows
+  }
+  const bool owner = kh == 0;  // the waves that finish and store the rows
   // ---- phase 3: global first-order correction --------------------------------------------
-  if (do_first) {
+  if (do_first && owner) {
     f32x16 T2[2];
     const float bt = beta * dm.scale;
     qk_tile<2>(hstage ? sK1 : sK0, 0, qreg, T2, lofs);  // H-bar^T rows 0..63
@@ -413,8 +488,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
   }
   if (block_fo) {
     // hand the unnormalised numerator and (reference, denominator) to the block first-order kernel
-    const uint32_t q = 32 * wave + l32;
-    if ((int)q < n_i) {
+    const uint32_t q = 32 * qg + l32;
+    if (owner && (int)q < n_i) {
       const size_t row = (size_t)h * dm.L + (size_t)i * B + q;
       float* orow = w.opart + row * 128;
 #pragma unroll
@@ -432,12 +507,11 @@ __global__ __launch_bounds__(BLK * 2, 2) void attend_bf16(Dims dm, Work w, const
     return;
   }
   // ---- epilogue: bf16 output rows via LDS (queries 0..63 in one array, 64..127 in the other) --
-  const int xs = do_first ? (hstage ^ 1) : 0;
   char* stg_lo = xs ? sK1 : sK0;
   char* stg_hi = xs ? sV1 : sV0;
   const float inv_l = 1.0f / lsum;
-  {
-    const uint32_t q = 32 * wave + l32;
+  if (owner) {
+    const uint32_t q = 32 * qg + l32;
     char* stg = q < 64 ? stg_lo : stg_hi;
     const uint32_t qr = q & 63;
 #pragma unroll
@@ -557,6 +631,16 @@ __global__ __launch_bounds__(BLK * 2, 1) void first_block_bf16(Dims dm, Work w, 
   }
   const float cs = dm.scale * kLog2e;
   const LaneOffsets lofs = lane_offsets(lane);
+  // q.c, c = the key centre the pooled centroids are stored relative to
+  float qc = 0.f;
+  {
+    const float* kcen = w.kc + (size_t)h * 128;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qc = fmaf((float)qreg[s][e], kcen[16 * s + 8 * hh + e], qc);
+    qc += __shfl_xor(qc, 32);
+  }
 
   auto step = [&](int u, auto stc) {
     constexpr int ST = decltype(stc)::value;
@@ -572,7 +656,7 @@ __global__ __launch_bounds__(BLK * 2, 1) void first_block_bf16(Dims dm, Work w, 
 #pragma unroll
       for (int e = 0; e < 8; ++e) a = fmaf((float)qreg[s][e], (float)kv[e], a);
     }
-    a += __shfl_xor(a, 32);
+    a += __shfl_xor(a, 32) + qc;
     const float wgt = __builtin_amdgcn_exp2f(fmaf(a, cs, -mref)) * dm.scale;
     f32x16 T[2];
     qk_tile<2>(ST ? sA1 : sA0, 0, qreg, T, lofs);  // (q H_j)[0..63]
@@ -641,7 +725,7 @@ hipError_t launch_attend_bf16(const Dims& dm, const Work& w, const void* Q, cons
   if (dm.B == 128)
     hipLaunchKernelGGL(attend_bf16<128>, dim3(items), dim3(256), 0, s, dm, w, q, k, v, o);
   else
-    hipLaunchKernelGGL(attend_bf16<64>, dim3(items), dim3(128), 0, s, dm, w, q, k, v, o);
+    hipLaunchKernelGGL(attend_bf16<64>, dim3(items), dim3(256), 0, s, dm, w, q, k, v, o);
   return hipGetLastError();
 }
 

@@ -130,9 +130,10 @@ __device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t r, char* lds, u
 
 // Per-lane global offset of a 16-row chunk copy. Instruction m (0..3) of a chunk covers chunk rows
 // 4 m .. 4 m + 3: lane l reads row 4 m + l / 16 at the swizzle's source chunk for stored chunk l % 16.
-// The row's 1024 m bytes are not included: the instruction offset adds them, and on a direct-to-LDS
-// load it moves the LDS destination by the same amount (both checked on gfx950 with an in-bounds
-// probe, as is that the buffer range check covers the scalar and instruction offsets).
+// The row's 1024 m bytes are not included: the instruction offset adds them (it counts in the
+// buffer range check, which compares vector plus instruction offset with num_records), and on a
+// direct-to-LDS load it moves the LDS destination by the same amount (checked on gfx950 with an
+// in-bounds probe).
 // What remains depends on m only through the swizzle. Transpose-read tiles swizzle by row & 3 =
 // l / 16, the same for every m. Row-read tiles swizzle by row & 15 = 4 m | l / 16, and XOR-ing the
 // chunk with 4 m flips bits 6..7 of the byte offset: instruction m's offset is m = 0's XOR 64 m.
@@ -144,8 +145,9 @@ __device__ __forceinline__ uint32_t chunk_lane(int lane) {
 }
 
 // Direct copy of one 16-row chunk (4 KB) global -> LDS from inline assembly: one m0 write, four
-// loads. lds = the chunk's LDS byte address, soff = its global byte offset within the resource,
-// v0 = chunk_lane<TR>(lane). Bytes past the resource's range are written as 0.
+// loads. lds = the chunk's LDS byte address, soff = a scalar byte offset added to every address
+// (0 where rows past the data must read as zeros: the range check then needs no assumption about
+// the scalar offset), v0 = chunk_lane<TR>(lane). Bytes past the resource's range are written as 0.
 // Issued from assembly because the compiler's wait-count insertion cannot tell direct-to-LDS copies
 // into one buffer from reads of another: after a copy through the builtin it makes every later LDS
 // read wait for the copy. From assembly it does not see the copy at all, so the caller waits for
@@ -186,15 +188,22 @@ __device__ __forceinline__ void copy_chunk_async(const u32x4& rsrc, uint32_t lds
   }
 }
 
-// Direct copy of a ROWS x 256 B tile (rsrc from rsrc_words) by NWAVES waves in 16-row chunks: wave w
-// copies chunks w, w + NWAVES, ...; v0 = chunk_lane<TR>(lane).
+// Direct copy of a ROWS x 256 B tile whose first `bytes` bytes at `base` are valid, by NWAVES waves
+// in 16-row chunks: wave w copies chunks w, w + NWAVES, ...; v0 = chunk_lane<TR>(lane). Each chunk
+// gets a buffer resource of its own that starts at the chunk and ends where the valid bytes end
+// (zero bytes past them), so the rows past the end are zeros by the buffer range check on the
+// vector and instruction offsets alone: a raw buffer (stride 0) returns 0 for every load whose
+// offset lies at or beyond num_records (CDNA4 ISA, buffer instructions, range checking).
 template <int ROWS, int NWAVES, bool TR>
-__device__ __forceinline__ void copy_tile_chunks(const u32x4& r, uint32_t lds, uint32_t v0, int wave) {
+__device__ __forceinline__ void copy_tile_chunks(const void* base, uint32_t bytes, uint32_t lds, uint32_t v0,
+                                                 int wave) {
   static_assert(ROWS % (16 * NWAVES) == 0, "tile rows must split into 16-row chunks over the waves");
 #pragma unroll
   for (int n = 0; n < ROWS / 16 / NWAVES; ++n) {
     const uint32_t c = n * NWAVES + wave;
-    copy_chunk_async<TR>(r, lds + 4096u * c, v0, 4096u * c);
+    const uint32_t start = 4096u * c;
+    copy_chunk_async<TR>(rsrc_words(static_cast<const char*>(base) + start, bytes > start ? bytes - start : 0u),
+                         lds + start, v0, 0u);
   }
 }
 

@@ -69,11 +69,13 @@ Layout workspace_layout(const Dims& dm) {
   l.hbar = take(H * d * d * 4);
   l.M = take(H * Nb * 4);
   if (dm.dtype == PISA_DTYPE_BF16) {
+    l.kpart = take(H * (size_t)dm.NC * d * 4);
+    l.kc = take(H * d * 4);
     l.kbar_lo = take(H * (size_t)dm.Nbp * d * 2);
     l.vbar_lo = take(H * (size_t)dm.Nbp * d * 2);
     l.hbarT_lo = take(H * d * d * 2);
   } else {
-    l.kbar_lo = l.vbar_lo = l.hbarT_lo = (size_t)-1;
+    l.kpart = l.kc = l.kbar_lo = l.vbar_lo = l.hbarT_lo = (size_t)-1;
   }
   l.idx = take(H * Nb * (size_t)dm.k * 4);
   if (pisa::block_first_order(dm)) {
@@ -98,6 +100,8 @@ Work workspace_pointers(const Dims& dm, void* base) {
   w.hbar = reinterpret_cast<float*>(b + l.hbar);
   w.M = reinterpret_cast<float*>(b + l.M);
   if (dm.dtype == PISA_DTYPE_BF16) {
+    w.kpart = reinterpret_cast<float*>(b + l.kpart);
+    w.kc = reinterpret_cast<float*>(b + l.kc);
     w.kbar_lo = b + l.kbar_lo;
     w.vbar_lo = b + l.vbar_lo;
     w.hbarT_lo = b + l.hbarT_lo;

@@ -43,7 +43,9 @@ struct Work {
   float* G;         // [H][NC][d][d] partial sums of H_j = K_j^T V_j - kbar_j (sum V_j)^T
   float* hbar;      // [H][d][d]    H-bar
   float* M;         // [H][Nb]      ||H_j - H-bar||_F
-  void* kbar_lo;    // bf16 [H][Nbp][d] centroids, zero rows past Nb      (bf16 path only)
+  float* kpart;     // [H][NC][d]   per-chunk sums of the block centroids    (bf16 path only)
+  float* kc;        // [H][d]       key centre: mean of the block centroids   (bf16 path only)
+  void* kbar_lo;    // bf16 [H][Nbp][d] centroid minus the key centre, zero rows past Nb (bf16 path only)
   void* vbar_lo;    // bf16 [H][Nbp][d] value means, zero rows past Nb    (bf16 path only)
   void* hbarT_lo;   // bf16 [H][d][d]   transpose of H-bar                (bf16 path only)
   int32_t* idx;     // [H][Nb][k]   ascending critical block indices
@@ -53,7 +55,7 @@ struct Work {
 };
 
 struct Layout {
-  size_t qbar, kbar, vsum, G, hbar, M, kbar_lo, vbar_lo, hbarT_lo, idx, hjT_lo, opart, ml, total;
+  size_t qbar, kbar, vsum, G, hbar, M, kpart, kc, kbar_lo, vbar_lo, hbarT_lo, idx, hjT_lo, opart, ml, total;
 };
 
 Layout workspace_layout(const Dims& dm);

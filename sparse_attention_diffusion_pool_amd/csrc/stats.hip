@@ -86,6 +86,7 @@ __global__ __launch_bounds__(256, 2) void stats_pass_bf16(Dims dm, Work w, const
   __shared__ __attribute__((aligned(1024))) char Vs[BLK * 256];
   __shared__ float red[4][128];  // per-wave column sums of Q
   __shared__ float svs[128];     // the current block's value sums
+  __shared__ float kcs[128];     // the chunk's sum of block centroids (row a owned by one lane)
   constexpr int QR = BLK / 16;   // Q rows (16-byte pieces) per thread
   const int h = blockIdx.y, c = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -97,6 +98,7 @@ __global__ __launch_bounds__(256, 2) void stats_pass_bf16(Dims dm, Work w, const
   for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x16{};
   const int p = tid & 15, rg = tid >> 4;  // column chunk (8 columns) and row group for the sums
   u32x4 qa[QR];
+  if (tid < 128) kcs[tid] = 0.f;  // first read after the first block's barriers
 
   auto rows_of = [&](int j) { return (j == dm.Nb - 1) ? dm.n_last : dm.B; };
   for (int j = j0; j < j1; ++j) {
@@ -134,7 +136,12 @@ __global__ __launch_bounds__(256, 2) void stats_pass_bf16(Dims dm, Work w, const
     // the product, the same row as acc[.][x]
     if (l32 == 0) {
 #pragma unroll
-      for (int x = 0; x < 16; ++x) w.kbar[ob + 32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3)] = ksum[x] * inv;
+      for (int x = 0; x < 16; ++x) {
+        const int a = 32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3);
+        const float kb = ksum[x] * inv;
+        w.kbar[ob + a] = kb;
+        kcs[a] += kb;
+      }
     }
     if (lane < 32) {
       w.vsum[ob + 32 * wave + lane] = vsum[0];
@@ -163,6 +170,14 @@ __global__ __launch_bounds__(256, 2) void stats_pass_bf16(Dims dm, Work w, const
       const int a = 32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3);
       G[a * 128 + 32 * ct + l32] = acc[ct][x];
     }
+  if (l32 == 0) {  // each row a was summed by this lane alone
+    float* kp = w.kpart + ((size_t)h * dm.NC + c) * 128;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const int a = 32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3);
+      kp[a] = kcs[a];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -487,15 +502,28 @@ __global__ __launch_bounds__(256) void stats_finalize(Dims dm, Work w) {
   const int e = x * 256 + tid;  // entry a * D + b
   const int a = e / D, b = e % D;
   const float* G = w.G + (size_t)h * dm.NC * D * D + e;
-  float g0 = 0.f, g1 = 0.f, g2 = 0.f, g3 = 0.f;
+  // bf16 path: the chunk sums of the block centroids (column tid % D) are added in the same loop,
+  // so their loads are in flight together with the partials of H-bar
+  const bool cen = dm.dtype == 0;
+  const float* kp = cen ? w.kpart + (size_t)h * dm.NC * D + (tid % D) : G;
+  float g0 = 0.f, g1 = 0.f, g2 = 0.f, g3 = 0.f, k0 = 0.f, k1 = 0.f, k2 = 0.f, k3 = 0.f;
   int c = 0;
   for (; c + 4 <= dm.NC; c += 4) {
     g0 += G[(size_t)c * D * D];
     g1 += G[(size_t)(c + 1) * D * D];
     g2 += G[(size_t)(c + 2) * D * D];
     g3 += G[(size_t)(c + 3) * D * D];
+    if (cen) {
+      k0 += kp[(size_t)c * D];
+      k1 += kp[(size_t)(c + 1) * D];
+      k2 += kp[(size_t)(c + 2) * D];
+      k3 += kp[(size_t)(c + 3) * D];
+    }
   }
-  for (; c < dm.NC; ++c) g0 += G[(size_t)c * D * D];
+  for (; c < dm.NC; ++c) {
+    g0 += G[(size_t)c * D * D];
+    if (cen) k0 += kp[(size_t)c * D];
+  }
   const float v = ((g0 + g1) + (g2 + g3)) / (float)dm.Nb;
   w.hbar[(size_t)h * D * D + e] = v;
   if (dm.dtype == 0) {
@@ -505,12 +533,17 @@ __global__ __launch_bounds__(256) void stats_finalize(Dims dm, Work w) {
     __bf16* kl = reinterpret_cast<__bf16*>(w.kbar_lo) + (size_t)h * dm.Nbp * D;
     __bf16* vl = reinterpret_cast<__bf16*>(w.vbar_lo) + (size_t)h * dm.Nbp * D;
     const int per = 256 / D;  // pooled rows per workgroup pass
+    const int cc = tid % D;
+    // key centre c = mean of the block centroids (chunk sums added in a fixed order). The bf16
+    // pooled centroids are stored relative to it: keys that share a large common component then
+    // keep their differences to bf16 precision, and the attention kernel adds q.c back in fp32.
+    const float kcen = ((k0 + k1) + (k2 + k3)) / (float)dm.Nb;
+    if (x == 0 && tid < D) w.kc[(size_t)h * D + cc] = kcen;
     for (int j = x * per + tid / D; j < dm.Nbp; j += gridDim.x * per) {
-      const int cc = tid % D;
       float kv = 0.f, vv = 0.f;
       if (j < dm.Nb) {
         const float n = (j == dm.Nb - 1) ? (float)dm.n_last : (float)dm.B;
-        kv = kb[(size_t)j * D + cc];
+        kv = kb[(size_t)j * D + cc] - kcen;
         vv = vs[(size_t)j * D + cc] / n;
       }
       kl[(size_t)j * D + cc] = (__bf16)kv;
