@@ -24,9 +24,10 @@ template <int D, int NS, int RPW>
 __global__ __launch_bounds__(256) void route_kernel(Dims dm, Work w) {
   constexpr int kRows = 4 * RPW;
   constexpr int kRowsPerWave = RPW;
+  // 16 query blocks per workgroup at d = 128: scores on the matrix unit; otherwise fp32 FMA
+  constexpr bool kMatrix = D == 128 && kRows == 16;
   constexpr int STR = D + 4;  // padded row stride (floats) of the LDS tiles
   __shared__ __attribute__((aligned(16))) float qs[kRows][STR];
-  __shared__ __attribute__((aligned(16))) float kt[64][STR];
   __shared__ float qn[kRows];
   const int h = blockIdx.y, i0 = blockIdx.x * kRows;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -50,63 +51,118 @@ __global__ __launch_bounds__(256) void route_kernel(Dims dm, Work w) {
   // key[][] is indexed with compile-time indices only (every loop over it is unrolled), so that it
   // stays in registers
   uint32_t key[kRowsPerWave][NS];
-  // The next centroid tile (this thread's share, and M_j of the lane's key) is loaded into
-  // registers while the current one is used, so one tile's load latency overlaps the previous
-  // tile's dot products instead of adding up load by load.
-  constexpr int kPer = 64 * (D / 4) / 256;  // 16-byte pieces of a tile per thread
-  f32x4 pre[kPer];
-  float mpre = 0.f;
-  auto fetch = [&](int jt) __attribute__((always_inline)) {
+  if constexpr (kMatrix) {
+    // Scores on the fp32 matrix unit (v_mfma_f32_16x16x4_f32): rows = the workgroup's 16 query
+    // blocks, columns = 16 keys per wave and tile of 64. The sum over d runs as 32 steps of 4
+    // with lane l covering d = 32 (l / 16) + t at step t (A: row l % 16, B: key l % 16), so each
+    // lane's operands are 32 consecutive floats of one row. Lane l then holds the scores of rows
+    // 4 (l / 16) .. + 3 for its key; they pass through LDS to the select layout (lane = key).
+    __shared__ float scl[16][65];
+    float qa[32];
+    {
+      const float* qrow = &qs[lane & 15][32 * (lane >> 4)];
 #pragma unroll
-    for (int it = 0; it < kPer; ++it) {
-      const int e = tid + 256 * it;
-      const int r = e / (D / 4), c4 = e % (D / 4);
-      pre[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (jt + r < Nb) pre[it] = *reinterpret_cast<const f32x4*>(kbar + (size_t)(jt + r) * D + 4 * c4);
+      for (int t4 = 0; t4 < 8; ++t4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(qrow + 4 * t4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qa[4 * t4 + e] = v[e];
+      }
     }
-    mpre = (jt + lane < Nb) ? M[jt + lane] : 0.f;
-  };
-  fetch(0);
+    f32x4 kb[8], kpre[8];
+    float mpre = 0.f;
+    auto fetch = [&](int jt) __attribute__((always_inline)) {
+      const int jk = jt + 16 * wave + (lane & 15);
+      const float* src = kbar + (size_t)jk * D + 32 * (lane >> 4);
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    __syncthreads();  // previous tile consumed (and qn visible on the first pass)
-    const int jt = 64 * s;
-    float mj = 0.f;
-    if (jt < Nb) {
+      for (int t4 = 0; t4 < 8; ++t4)
+        kpre[t4] = jk < Nb ? *reinterpret_cast<const f32x4*>(src + 4 * t4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      mpre = jk < Nb ? M[jk] : 0.f;
+    };
+    fetch(0);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int jt = 64 * s;
+#pragma unroll
+      for (int t4 = 0; t4 < 8; ++t4) kb[t4] = kpre[t4];
+      const float mj = mpre;
+      if (jt + 64 < Nb) fetch(jt + 64);
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 32; ++t) c = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[t], kb[t >> 2][t & 3], c, 0, 0, 0);
+      const int jk = jt + 16 * wave + (lane & 15);
+      const float nj = (jk == Nb - 1) ? (float)dm.n_last : (float)dm.B;
+      __syncthreads();  // previous tile's scores read (and qn visible on the first pass)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float sc = c[r];
+        if (dm.routing == 0) sc += logf(fmaf(qn[4 * (lane >> 4) + r], mj, nj));
+        scl[4 * (lane >> 4) + r][16 * wave + (lane & 15)] = sc;
+      }
+      __syncthreads();
+      const bool valid = jt + lane < Nb;
+#pragma unroll
+      for (int r = 0; r < kRowsPerWave; ++r) key[r][s] = valid ? float_order_key(scl[kRowsPerWave * wave + r][lane]) : 0u;
+    }
+  } else {
+    __shared__ __attribute__((aligned(16))) float kt[64][STR];
+    // The next centroid tile (this thread's share, and M_j of the lane's key) is loaded into
+    // registers while the current one is used, so one tile's load latency overlaps the previous
+    // tile's dot products instead of adding up load by load.
+    constexpr int kPer = 64 * (D / 4) / 256;  // 16-byte pieces of a tile per thread
+    f32x4 pre[kPer];
+    float mpre = 0.f;
+    auto fetch = [&](int jt) __attribute__((always_inline)) {
 #pragma unroll
       for (int it = 0; it < kPer; ++it) {
         const int e = tid + 256 * it;
         const int r = e / (D / 4), c4 = e % (D / 4);
-        *reinterpret_cast<f32x4*>(&kt[r][4 * c4]) = pre[it];
+        pre[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (jt + r < Nb) pre[it] = *reinterpret_cast<const f32x4*>(kbar + (size_t)(jt + r) * D + 4 * c4);
       }
-      mj = mpre;
-      if (jt + 64 < Nb) fetch(jt + 64);
-    }
-    __syncthreads();
-    const int j = jt + lane;
-    float acc[kRowsPerWave];
+      mpre = (jt + lane < Nb) ? M[jt + lane] : 0.f;
+    };
+    fetch(0);
 #pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r) acc[r] = 0.f;
-    if (jt < Nb) {
-      for (int c4 = 0; c4 < D / 4; ++c4) {
-        const f32x4 kv = *reinterpret_cast<const f32x4*>(&kt[lane][4 * c4]);
+    for (int s = 0; s < NS; ++s) {
+      __syncthreads();  // previous tile consumed (and qn visible on the first pass)
+      const int jt = 64 * s;
+      float mj = 0.f;
+      if (jt < Nb) {
 #pragma unroll
-        for (int r = 0; r < kRowsPerWave; ++r) {
-          const f32x4 qv = *reinterpret_cast<const f32x4*>(&qs[kRowsPerWave * wave + r][4 * c4]);
-          acc[r] = fmaf(qv[0], kv[0], acc[r]);
-          acc[r] = fmaf(qv[1], kv[1], acc[r]);
-          acc[r] = fmaf(qv[2], kv[2], acc[r]);
-          acc[r] = fmaf(qv[3], kv[3], acc[r]);
+        for (int it = 0; it < kPer; ++it) {
+          const int e = tid + 256 * it;
+          const int r = e / (D / 4), c4 = e % (D / 4);
+          *reinterpret_cast<f32x4*>(&kt[r][4 * c4]) = pre[it];
+        }
+        mj = mpre;
+        if (jt + 64 < Nb) fetch(jt + 64);
+      }
+      __syncthreads();
+      const int j = jt + lane;
+      float acc[kRowsPerWave];
+#pragma unroll
+      for (int r = 0; r < kRowsPerWave; ++r) acc[r] = 0.f;
+      if (jt < Nb) {
+        for (int c4 = 0; c4 < D / 4; ++c4) {
+          const f32x4 kv = *reinterpret_cast<const f32x4*>(&kt[lane][4 * c4]);
+#pragma unroll
+          for (int r = 0; r < kRowsPerWave; ++r) {
+            const f32x4 qv = *reinterpret_cast<const f32x4*>(&qs[kRowsPerWave * wave + r][4 * c4]);
+            acc[r] = fmaf(qv[0], kv[0], acc[r]);
+            acc[r] = fmaf(qv[1], kv[1], acc[r]);
+            acc[r] = fmaf(qv[2], kv[2], acc[r]);
+            acc[r] = fmaf(qv[3], kv[3], acc[r]);
+          }
         }
       }
-    }
-    const bool valid = j < Nb;
-    const float nj = (j == Nb - 1) ? (float)dm.n_last : (float)dm.B;
+      const bool valid = j < Nb;
+      const float nj = (j == Nb - 1) ? (float)dm.n_last : (float)dm.B;
 #pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r) {
-      float sc = acc[r];
-      if (dm.routing == 0) sc += logf(fmaf(qn[kRowsPerWave * wave + r], mj, nj));
-      key[r][s] = valid ? float_order_key(sc) : 0u;
+      for (int r = 0; r < kRowsPerWave; ++r) {
+        float sc = acc[r];
+        if (dm.routing == 0) sc += logf(fmaf(qn[kRowsPerWave * wave + r], mj, nj));
+        key[r][s] = valid ? float_order_key(sc) : 0u;
+      }
     }
   }
 
@@ -123,6 +179,8 @@ __global__ __launch_bounds__(256) void route_kernel(Dims dm, Work w) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) cnt += __popcll(__ballot(key[r][s] >= cand));
       if (cnt >= kk) T = cand;
+      // exactly k keys at or above cand: they are the k largest, whatever the lower bits decide
+      if (cnt == kk) break;
     }
     int gt = 0;
 #pragma unroll
