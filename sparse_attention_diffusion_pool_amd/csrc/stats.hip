@@ -392,6 +392,62 @@ __global__ __launch_bounds__(256) void stats_cov_bf16(Dims dm, Work w, const __b
   if (tid == 0) w.M[(size_t)h * dm.Nb + j] = sqrtf(red[0] + red[1] + red[2] + red[3]);
 }
 
+// Covariance pass, Frobenius M_j (the default): one workgroup per chunk of dm.chunk blocks, like the
+// statistics pass, with the lane's 64 entries of H-bar held in registers for the whole chunk (one
+// load per entry per workgroup instead of one per entry and block), and the centroid and value-sum
+// factors of the correction read per block. One LDS stage; two workgroups per CU, so one
+// workgroup's block is in flight while the other multiplies.
+template <int BLK>
+__global__ __launch_bounds__(256, 2) void stats_cov_chunk_bf16(Dims dm, Work w, const __bf16* __restrict__ K,
+                                                               const __bf16* __restrict__ V) {
+  __shared__ __attribute__((aligned(1024))) char Ks[BLK * 256];
+  __shared__ __attribute__((aligned(1024))) char Vs[BLK * 256];
+  __shared__ float red[2][4];
+  const int h = blockIdx.y, c = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int j0 = c * dm.chunk, j1 = min(dm.Nb, j0 + dm.chunk);
+  const float* hb = w.hbar + (size_t)h * 128 * 128;
+  float hbr[4][16];  // H-bar[a][b] for the lane's accumulator entries (a, b as in acc[ct][x])
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int x = 0; x < 16; ++x)
+      hbr[ct][x] = hb[(32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3)) * 128 + 32 * ct + l32];
+  for (int j = j0; j < j1; ++j) {
+    const int n = (j == dm.Nb - 1) ? dm.n_last : dm.B;
+    const size_t r0 = (size_t)h * dm.L * 128 + (size_t)j * dm.B * 128;
+    tile_to_lds<true>(make_rsrc(K + r0, n * 256), 256, Ks, BLK, wave, 4, lane);
+    tile_to_lds<true>(make_rsrc(V + r0, n * 256), 256, Vs, BLK, wave, 4, lane);
+    const float* kb = w.kbar + ((size_t)h * dm.Nb + j) * 128;
+    const float* vs = w.vsum + ((size_t)h * dm.Nb + j) * 128;
+    float ka[16], vb[4];
+#pragma unroll
+    for (int x = 0; x < 16; ++x) ka[x] = kb[32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3)];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) vb[ct] = vs[32 * ct + l32];
+    wait_vmem();
+    __syncthreads();  // the block's tiles landed
+    f32x16 acc[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x16{};
+    ktv_mfma<BLK>(Ks, Vs, acc, wave, lane);
+    float ss = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const float hv = fmaf(-ka[x], vb[ct], acc[ct][x]) - hbr[ct][x];
+        ss = fmaf(hv, hv, ss);
+      }
+    ss = wave_sum(ss);
+    if (lane == 0) red[j & 1][wave] = ss;
+    __syncthreads();  // every wave done with the tiles; the block's partial sums visible
+    if (tid == 0) w.M[(size_t)h * dm.Nb + j] = sqrtf(red[j & 1][0] + red[j & 1][1] + red[j & 1][2] + red[j & 1][3]);
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // fp32 inputs: plain FMA. Each thread owns a P x P patch of the D x D product (P = D / 16).
 // ---------------------------------------------------------------------------------------------
@@ -574,6 +630,14 @@ hipError_t launch_stats_cov_bf16(const Dims& dm, const Work& w, const void* K, c
 #define PISA_COV(BLK, SPEC, HJT) \
   hipLaunchKernelGGL((stats_cov_bf16<BLK, SPEC, HJT>), grid, dim3(256), 0, s, dm, w, k, v)
   const bool hjt = block_first_order(dm);
+  if (!dm.spectral && !hjt) {
+    dim3 cgrid(dm.NC, dm.H);
+    if (dm.B == 128)
+      hipLaunchKernelGGL(stats_cov_chunk_bf16<128>, cgrid, dim3(256), 0, s, dm, w, k, v);
+    else
+      hipLaunchKernelGGL(stats_cov_chunk_bf16<64>, cgrid, dim3(256), 0, s, dm, w, k, v);
+    return hipGetLastError();
+  }
   if (dm.B == 128) {
     if (dm.spectral) {
       if (hjt) PISA_COV(128, true, true); else PISA_COV(128, true, false);
