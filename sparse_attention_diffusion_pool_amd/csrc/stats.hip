@@ -8,8 +8,9 @@
 // (pooled scaled query, key centroid, value sum) and the partial sum of the block first-order
 // matrices over its blocks, H_j = K_j^T V_j - kbar_j (sum V_j)^T (= sum_n (k_n - kbar_j)^T v_n).
 // Finalize (per head): H-bar = (sum of the partials) / N_b; bf16 copies of the pooled tokens and
-// of H-bar^T for the attention kernel. Covariance pass (one workgroup per block): H_j again, then
-// M_j = ||H_j - H-bar||_F (and H_j^T in bf16 for the block-wise first-order variant).
+// of H-bar^T for the attention kernel. Covariance pass (one workgroup per chunk of blocks for the
+// Frobenius norm, one per block for the spectral norm and the H_j^T variant): H_j again, then
+// M_j = ||H_j - H-bar|| (and H_j^T in bf16 for the block-wise first-order variant).
 //
 // bf16 inputs: K_j^T V_j on v_mfma_f32_32x32x16_bf16 (products of bf16 values are exact in fp32,
 // accumulation fp32); both operands come from row-major LDS tiles through ds_read_b64_tr_b16.
@@ -44,9 +45,10 @@ __device__ __forceinline__ void ktv_mfma(const char* Ks, const char* Vs, f32x16 
   }
 }
 
-// The same product, plus the block's column sums on the matrix unit: ksum = K^T 1 (the K^T operand
-// against a ones operand) and vsum = 1^T V for the wave's own 32 columns. Products with 1.0 are
-// exact and the sums accumulate in fp32. Rows past the block end are zero in the tiles.
+// The same product, plus the column sums on the matrix unit: ksum += K^T 1 (the K^T operand
+// against a ones operand) and vsum += 1^T V for the wave's own 32 columns, over the BLK rows of the
+// tiles (acc, ksum and vsum accumulate; the caller clears them). Products with 1.0 are exact and
+// the sums accumulate in fp32. Rows past the block end are zero in the tiles.
 // Lane l holds: ksum[x] = column sum of K for d = 32 wave + 8 (x >> 2) + 4 (l >> 5) + (x & 3);
 // vsum[0] = column sum of V for column 32 wave + (l & 31).
 template <int BLK>
@@ -56,8 +58,6 @@ __device__ __forceinline__ void ktv_mfma_sums(const char* Ks, const char* Vs, f3
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
-  ksum = f32x16{};
-  vsum = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < BLK / 16; ++ks) {
     const uint32_t klo = 16 * ks + 8 * hh;
@@ -73,97 +73,176 @@ __device__ __forceinline__ void ktv_mfma_sums(const char* Ks, const char* Vs, f3
   }
 }
 
-// Pass A, bf16. One LDS stage (64 KB) and two workgroups per CU: each workgroup copies a block's K
-// and V tiles to LDS (Q rows into registers), then sums and multiplies them, while the other
-// workgroup on the CU has its block in flight. (Two stages in one workgroup would keep only one
-// block in flight per CU: LDS holds about two blocks.) The chunk's partial is corrected by the
-// centroids block by block: G_c = sum_{j in c} (K_j^T V_j - kbar_j (sum V_j)^T) = sum_{j in c} H_j.
+// Q column sums, bf16 (the pooled scaled query of every block): one workgroup per block, each thread
+// summing 16-byte pieces of its rows in registers, then across the 16-lane row groups and across
+// waves. A plain streaming reduction with many small workgroups per CU.
 template <int BLK>
-__global__ __launch_bounds__(256, 2) void stats_pass_bf16(Dims dm, Work w, const __bf16* __restrict__ Q,
-                                                          const __bf16* __restrict__ K,
+__global__ __launch_bounds__(256) void stats_qbar_bf16(Dims dm, Work w, const __bf16* __restrict__ Q) {
+  __shared__ float red[4][128];
+  constexpr int QR = BLK / 16;  // 16-byte pieces per thread
+  const int h = blockIdx.y, j = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int p = tid & 15, rg = tid >> 4;  // column chunk (8 columns) and row group
+  const int n = (j == dm.Nb - 1) ? dm.n_last : dm.B;
+  const size_t r0 = (size_t)h * dm.L * 128 + (size_t)j * dm.B * 128;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + r0, n * 256);
+  u32x4 qa[QR];
+#pragma unroll
+  for (int e = 0; e < QR; ++e) qa[e] = buf_load16(rq, (rg + 16 * e) * 256 + p * 16);
+  float qs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int e = 0; e < QR; ++e) {
+    float f[8];
+    unpack_bf16x8(qa[e], f);
+    for (int x = 0; x < 8; ++x) qs[x] += f[x];
+  }
+  for (int x = 0; x < 8; ++x) {
+    qs[x] += __shfl_xor(qs[x], 16);
+    qs[x] += __shfl_xor(qs[x], 32);
+  }
+  if (lane < 16)
+    for (int x = 0; x < 8; ++x) red[wave][8 * p + x] = qs[x];
+  __syncthreads();
+  if (tid < 128)
+    w.qbar[((size_t)h * dm.Nb + j) * 128 + tid] =
+        (red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid]) * dm.scale * (1.0f / (float)n);
+}
+
+// The statistics pass and the covariance pass (bf16) stream a block's K and V tiles through LDS
+// in two halves of BLK/2 rows (the half-block ring): half h of the next block is copied into half
+// h's slots as soon as every wave has read half h of the current block, so one half is in flight
+// while the other is multiplied, and a CU (two workgroups, 64 KB of slots each) always has copies
+// outstanding. A half starts at a row that is a multiple of 16, so the tiles' swizzle is the same
+// as for the whole block; rows of a half past the block end are written as zeros (each 16-row
+// chunk's buffer resource ends where the block's rows end).
+//
+// The copies are issued from assembly (copy_tile_chunks), out of sight of the compiler's
+// wait-count insertion, which cannot tell copies into one slot from reads of the other and would
+// make every read wait for the latest copy. The loops issue no other global loads, so the waits
+// below (for all but the copies of the half issued after the one needed) are the only ones.
+template <int BLK>
+__device__ __forceinline__ void kv_half_copy(const __bf16* K, const __bf16* V, size_t r0, int n, int half,
+                                             uint32_t kslot, uint32_t vslot, uint32_t v0, int wave) {
+  constexpr int HR = BLK / 2;
+  const uint32_t bytes = 256u * (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(HR, n - HR * half)));
+  const __bf16* kb = K + r0 + (size_t)HR * half * 128;
+  const __bf16* vb = V + r0 + (size_t)HR * half * 128;
+  if constexpr (HR % 64 == 0) {  // every wave copies a chunk of K and one of V
+    copy_tile_chunks<HR, 4, true>(kb, bytes, kslot, v0, wave);
+    copy_tile_chunks<HR, 4, true>(vb, bytes, vslot, v0, wave);
+  } else {  // 32-row halves: waves 0-1 copy K's two chunks, waves 2-3 V's
+    static_assert(HR == 32, "half-block rows");
+    if (wave < 2) copy_tile_chunks<HR, 2, true>(kb, bytes, kslot, v0, wave);
+    else copy_tile_chunks<HR, 2, true>(vb, bytes, vslot, v0, wave - 2);
+  }
+}
+
+// Copy instructions each thread issues per half (4 per 16-row chunk).
+template <int BLK>
+constexpr int kv_half_vmem() { return (BLK / 2) % 64 == 0 ? 2 * (BLK / 2) / 16 : 4; }
+
+// Workgroup barrier that orders LDS accesses only: each wave's LDS reads and writes have completed
+// (lgkmcnt(0)) before any wave passes. Unlike __syncthreads() it does not wait for the wave's
+// outstanding copies and stores, so the ring's next half stays in flight across it. The "memory"
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N), expcnt and lgkmcnt at their maxima (N < 16). Vector-memory operations
+// complete in issue order, so this waits for everything issued before the N most recent.
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// Pass A, bf16: column sums of K and V and K^T V (matrix unit, from LDS) over the chunk's blocks,
+// through the half-block ring. The chunk's partial is corrected by the centroids block by block:
+// G_c = sum_{j in c} (K_j^T V_j - kbar_j (sum V_j)^T) = sum_{j in c} H_j. The Q column sums are
+// stats_qbar_bf16's.
+template <int BLK>
+__global__ __launch_bounds__(256, 2) void stats_pass_bf16(Dims dm, Work w, const __bf16* __restrict__ K,
                                                           const __bf16* __restrict__ V) {
-  __shared__ __attribute__((aligned(1024))) char Ks[BLK * 256];
-  __shared__ __attribute__((aligned(1024))) char Vs[BLK * 256];
-  __shared__ float red[4][128];  // per-wave column sums of Q
-  __shared__ float svs[128];     // the current block's value sums
-  __shared__ float kcs[128];     // the chunk's sum of block centroids (row a owned by one lane)
-  constexpr int QR = BLK / 16;   // Q rows (16-byte pieces) per thread
+  __shared__ __attribute__((aligned(1024))) char Ks0[BLK * 128];  // half-block slots
+  __shared__ __attribute__((aligned(1024))) char Ks1[BLK * 128];
+  __shared__ __attribute__((aligned(1024))) char Vs0[BLK * 128];
+  __shared__ __attribute__((aligned(1024))) char Vs1[BLK * 128];
+  __shared__ float svs[128];  // the current block's value sums
+  __shared__ float kcs[128];  // the chunk's sum of block centroids (row a owned by one lane)
+  constexpr int HR = BLK / 2;
+  constexpr int NV = kv_half_vmem<BLK>();
   const int h = blockIdx.y, c = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j0 = c * dm.chunk, j1 = min(dm.Nb, j0 + dm.chunk);
   const size_t head = (size_t)h * dm.L * 128;
   const uint32_t hh = lane >> 5, l32 = lane & 31;
+  const uint32_t v0 = chunk_lane<true>(lane);
+  const uint32_t k0 = lds_addr(Ks0), k1 = lds_addr(Ks1), s0 = lds_addr(Vs0), s1 = lds_addr(Vs1);
   f32x16 acc[4];
   for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x16{};
-  const int p = tid & 15, rg = tid >> 4;  // column chunk (8 columns) and row group for the sums
-  u32x4 qa[QR];
   if (tid < 128) kcs[tid] = 0.f;  // first read after the first block's barriers
 
   auto rows_of = [&](int j) { return (j == dm.Nb - 1) ? dm.n_last : dm.B; };
-  for (int j = j0; j < j1; ++j) {
-    const int n = rows_of(j);
-    const size_t r0 = head + (size_t)j * dm.B * 128;
-    tile_to_lds<true>(make_rsrc(K + r0, n * 256), 256, Ks, BLK, wave, 4, lane);
-    tile_to_lds<true>(make_rsrc(V + r0, n * 256), 256, Vs, BLK, wave, 4, lane);
-    {
-      const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + r0, n * 256);
-#pragma unroll
-      for (int e = 0; e < QR; ++e) qa[e] = buf_load16(rq, (rg + 16 * e) * 256 + p * 16);
-    }
-    wait_vmem();
-    __syncthreads();  // the block's tiles landed
-    const float inv = 1.0f / (float)n;
-    const size_t ob = ((size_t)h * dm.Nb + j) * 128;
-    // Q (in registers): VALU sums over this thread's rows, then across the 16-lane row groups
-    float qs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int e = 0; e < QR; ++e) {
-      float f[8];
-      unpack_bf16x8(qa[e], f);
-      for (int x = 0; x < 8; ++x) qs[x] += f[x];
-    }
-    for (int x = 0; x < 8; ++x) {
-      qs[x] += __shfl_xor(qs[x], 16);
-      qs[x] += __shfl_xor(qs[x], 32);
-    }
-    if (lane < 16)
-      for (int x = 0; x < 8; ++x) red[wave][8 * p + x] = qs[x];
-    // K and V (in LDS): column sums on the matrix unit beside K^T V
-    f32x16 ksum, vsum;
-    ktv_mfma_sums<BLK>(Ks, Vs, acc, ksum, vsum, wave, lane);
-    // lane l's ksum[x] is the column sum of K for row a = 32 wave + 8 (x >> 2) + 4 hh + (x & 3) of
-    // the product, the same row as acc[.][x]
+  auto issue = [&](int j, int half) __attribute__((always_inline)) {
+    kv_half_copy<BLK>(K, V, head + (size_t)j * dm.B * 128, rows_of(j), half, half ? k1 : k0, half ? s1 : s0, v0,
+                      wave);
+  };
+  // a block's outputs are stored after the next block's first barrier (or after the loop): the
+  // copies then stay the most recent vector-memory operations at every wait
+  float pk[16], pv = 0.f;
+  size_t pob = 0;
+  auto store_pending = [&]() __attribute__((always_inline)) {
     if (l32 == 0) {
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int a = 32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3);
-        const float kb = ksum[x] * inv;
-        w.kbar[ob + a] = kb;
-        kcs[a] += kb;
-      }
+      for (int x = 0; x < 16; ++x) w.kbar[pob + 32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3)] = pk[x];
     }
-    if (lane < 32) {
-      w.vsum[ob + 32 * wave + lane] = vsum[0];
-      svs[32 * wave + lane] = vsum[0];
+    if (lane < 32) w.vsum[pob + 32 * wave + lane] = pv;
+  };
+  if (j0 < j1) {
+    issue(j0, 0);
+    issue(j0, 1);
+  }
+  for (int j = j0; j < j1; ++j) {
+    const int n = rows_of(j);
+    const bool more = j + 1 < j1;
+    f32x16 ksum = f32x16{}, vsum = f32x16{};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      // half (j, half) landed; the half issued after it, if any, stays in flight
+      if (half == 0 || more) wait_vmem_but<NV>(); else wait_vmem();
+      lds_barrier();
+      if (half == 0 && j > j0) store_pending();
+      ktv_mfma_sums<HR>(half ? Ks1 : Ks0, half ? Vs1 : Vs0, acc, ksum, vsum, wave, lane);
+      lds_barrier();  // every wave done with this half's slots
+      if (more) issue(j + 1, half);
     }
-    __syncthreads();  // red and svs complete; every wave done with the tiles
-    if (tid < 128) {
-      const float sq = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
-      w.qbar[ob + tid] = sq * dm.scale * inv;
+    const float inv = 1.0f / (float)n;
+    pob = ((size_t)h * dm.Nb + j) * 128;
+    // lane l's ksum[x] is the column sum of K for row a = 32 wave + 8 (x >> 2) + 4 hh + (x & 3) of
+    // the product, the same row as acc[.][x]
+#pragma unroll
+    for (int x = 0; x < 16; ++x) pk[x] = ksum[x] * inv;
+    if (l32 == 0) {
+#pragma unroll
+      for (int x = 0; x < 16; ++x) kcs[32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3)] += pk[x];
     }
+    pv = vsum[0];
+    if (lane < 32) svs[32 * wave + lane] = pv;
+    lds_barrier();  // svs complete (next written after the next block's first barrier)
     // acc[ct][x] -= kbar_j[a] vsum_j[b], b = 32 ct + l32
     float vb[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) vb[ct] = svs[32 * ct + l32];
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
-      const float ka = ksum[x] * inv;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) acc[ct][x] = fmaf(-ka, vb[ct], acc[ct][x]);
+      for (int ct = 0; ct < 4; ++ct) acc[ct][x] = fmaf(-pk[x], vb[ct], acc[ct][x]);
     }
-    __syncthreads();  // red and svs read before the next block overwrites them
   }
+  if (j0 < j1) store_pending();
   float* G = w.G + ((size_t)h * dm.NC + c) * 128 * 128;
   for (int ct = 0; ct < 4; ++ct)
     for (int x = 0; x < 16; ++x) {
@@ -393,21 +472,38 @@ __global__ __launch_bounds__(256) void stats_cov_bf16(Dims dm, Work w, const __b
 }
 
 // Covariance pass, Frobenius M_j (the default): one workgroup per chunk of dm.chunk blocks, like the
-// statistics pass, with the lane's 64 entries of H-bar held in registers for the whole chunk (one
-// load per entry per workgroup instead of one per entry and block), and the centroid and value-sum
-// factors of the correction read per block. One LDS stage; two workgroups per CU, so one
-// workgroup's block is in flight while the other multiplies.
+// statistics pass and through the same half-block ring, with the lane's 64 entries of H-bar held in
+// registers for the whole chunk. The block's centroid and value sums are formed again on the
+// matrix unit beside K^T V (the same instructions in the same order as the statistics pass, so the
+// same values) rather than read back: the loop then issues no global loads besides the copies.
 template <int BLK>
 __global__ __launch_bounds__(256, 2) void stats_cov_chunk_bf16(Dims dm, Work w, const __bf16* __restrict__ K,
                                                                const __bf16* __restrict__ V) {
-  __shared__ __attribute__((aligned(1024))) char Ks[BLK * 256];
-  __shared__ __attribute__((aligned(1024))) char Vs[BLK * 256];
+  __shared__ __attribute__((aligned(1024))) char Ks0[BLK * 128];  // half-block slots
+  __shared__ __attribute__((aligned(1024))) char Ks1[BLK * 128];
+  __shared__ __attribute__((aligned(1024))) char Vs0[BLK * 128];
+  __shared__ __attribute__((aligned(1024))) char Vs1[BLK * 128];
+  __shared__ float svs[2][128];  // value sums of the block (alternating buffers)
   __shared__ float red[2][4];
+  constexpr int HR = BLK / 2;
+  constexpr int NV = kv_half_vmem<BLK>();
   const int h = blockIdx.y, c = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, l32 = lane & 31;
   const int j0 = c * dm.chunk, j1 = min(dm.Nb, j0 + dm.chunk);
+  const size_t head = (size_t)h * dm.L * 128;
+  const uint32_t v0 = chunk_lane<true>(lane);
+  const uint32_t k0 = lds_addr(Ks0), k1 = lds_addr(Ks1), s0 = lds_addr(Vs0), s1 = lds_addr(Vs1);
+  auto rows_of = [&](int j) { return (j == dm.Nb - 1) ? dm.n_last : dm.B; };
+  auto issue = [&](int j, int half) __attribute__((always_inline)) {
+    kv_half_copy<BLK>(K, V, head + (size_t)j * dm.B * 128, rows_of(j), half, half ? k1 : k0, half ? s1 : s0, v0,
+                      wave);
+  };
+  if (j0 < j1) {
+    issue(j0, 0);
+    issue(j0, 1);
+  }
   const float* hb = w.hbar + (size_t)h * 128 * 128;
   float hbr[4][16];  // H-bar[a][b] for the lane's accumulator entries (a, b as in acc[ct][x])
 #pragma unroll
@@ -416,35 +512,49 @@ __global__ __launch_bounds__(256, 2) void stats_cov_chunk_bf16(Dims dm, Work w, 
     for (int x = 0; x < 16; ++x)
       hbr[ct][x] = hb[(32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3)) * 128 + 32 * ct + l32];
   for (int j = j0; j < j1; ++j) {
-    const int n = (j == dm.Nb - 1) ? dm.n_last : dm.B;
-    const size_t r0 = (size_t)h * dm.L * 128 + (size_t)j * dm.B * 128;
-    tile_to_lds<true>(make_rsrc(K + r0, n * 256), 256, Ks, BLK, wave, 4, lane);
-    tile_to_lds<true>(make_rsrc(V + r0, n * 256), 256, Vs, BLK, wave, 4, lane);
-    const float* kb = w.kbar + ((size_t)h * dm.Nb + j) * 128;
-    const float* vs = w.vsum + ((size_t)h * dm.Nb + j) * 128;
-    float ka[16], vb[4];
-#pragma unroll
-    for (int x = 0; x < 16; ++x) ka[x] = kb[32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3)];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) vb[ct] = vs[32 * ct + l32];
-    wait_vmem();
-    __syncthreads();  // the block's tiles landed
+    const bool more = j + 1 < j1;
     f32x16 acc[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x16{};
-    ktv_mfma<BLK>(Ks, Vs, acc, wave, lane);
+    f32x16 ksum = f32x16{}, vsum = f32x16{};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      // half (j, half) landed; the half issued after it, if any, stays in flight (the stores
+      // issued since are younger still). The first block waits for everything: the H-bar loads
+      // above are then complete, and the compiler, which does not count the copies, inserts no
+      // wait of its own for them later.
+      if (half == 0 && j == j0) wait_vmem();
+      else if (half == 0 || more) wait_vmem_but<NV>();
+      else wait_vmem();
+      lds_barrier();
+      if (half == 0 && j > j0 && tid == 0)  // M of the previous block (partials written before the barrier)
+        w.M[(size_t)h * dm.Nb + j - 1] =
+            sqrtf(red[(j - 1) & 1][0] + red[(j - 1) & 1][1] + red[(j - 1) & 1][2] + red[(j - 1) & 1][3]);
+      ktv_mfma_sums<HR>(half ? Ks1 : Ks0, half ? Vs1 : Vs0, acc, ksum, vsum, wave, lane);
+      lds_barrier();  // every wave done with this half's slots
+      if (more) issue(j + 1, half);
+    }
+    const float inv = 1.0f / (float)rows_of(j);
+    if (lane < 32) svs[j & 1][32 * wave + lane] = vsum[0];
+    lds_barrier();  // svs[j & 1] complete; it is next written two blocks on, after several barriers
     float ss = 0.f;
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
+    for (int ct = 0; ct < 4; ++ct) {
+      const float vb = svs[j & 1][32 * ct + l32];
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
-        const float hv = fmaf(-ka[x], vb[ct], acc[ct][x]) - hbr[ct][x];
+        const float hv = fmaf(-(ksum[x] * inv), vb, acc[ct][x]) - hbr[ct][x];
         ss = fmaf(hv, hv, ss);
       }
+    }
     ss = wave_sum(ss);
-    if (lane == 0) red[j & 1][wave] = ss;
-    __syncthreads();  // every wave done with the tiles; the block's partial sums visible
-    if (tid == 0) w.M[(size_t)h * dm.Nb + j] = sqrtf(red[j & 1][0] + red[j & 1][1] + red[j & 1][2] + red[j & 1][3]);
+    if (lane == 0) red[j & 1][wave] = ss;  // read after the next block's first barrier
+  }
+  if (j0 < j1) {
+    lds_barrier();
+    if (tid == 0)
+      w.M[(size_t)h * dm.Nb + j1 - 1] =
+          sqrtf(red[(j1 - 1) & 1][0] + red[(j1 - 1) & 1][1] + red[(j1 - 1) & 1][2] + red[(j1 - 1) & 1][3]);
   }
 }
 
@@ -612,14 +722,17 @@ __global__ __launch_bounds__(256) void stats_finalize(Dims dm, Work w) {
 
 hipError_t launch_stats_pass_bf16(const Dims& dm, const Work& w, const void* Q, const void* K, const void* V,
                                   hipStream_t s) {
-  dim3 grid(dm.NC, dm.H);
+  dim3 grid(dm.NC, dm.H), qgrid(dm.Nb, dm.H);
   auto q = static_cast<const __bf16*>(Q);
   auto k = static_cast<const __bf16*>(K);
   auto v = static_cast<const __bf16*>(V);
-  if (dm.B == 128)
-    hipLaunchKernelGGL(stats_pass_bf16<128>, grid, dim3(256), 0, s, dm, w, q, k, v);
-  else
-    hipLaunchKernelGGL(stats_pass_bf16<64>, grid, dim3(256), 0, s, dm, w, q, k, v);
+  if (dm.B == 128) {
+    hipLaunchKernelGGL(stats_qbar_bf16<128>, qgrid, dim3(256), 0, s, dm, w, q);
+    hipLaunchKernelGGL(stats_pass_bf16<128>, grid, dim3(256), 0, s, dm, w, k, v);
+  } else {
+    hipLaunchKernelGGL(stats_qbar_bf16<64>, qgrid, dim3(256), 0, s, dm, w, q);
+    hipLaunchKernelGGL(stats_pass_bf16<64>, grid, dim3(256), 0, s, dm, w, k, v);
+  }
   return hipGetLastError();
 }
 
