@@ -172,8 +172,27 @@ __global__ __launch_bounds__(256) void route_kernel(Dims dm, Work w) {
   for (int r = 0; r < kRowsPerWave; ++r) {
     const int i = i0 + kRowsPerWave * wave + r;
     if (i >= Nb) break;  // uniform per wave
-    uint32_t T = 0;
-    for (int b = 31; b >= 0; --b) {
+    // Every valid key lies between the row's smallest and largest, so all of them share the bits
+    // above the highest bit where those two differ: the k-th largest has them too, and the
+    // select starts below them (the same T as starting at bit 31, in fewer rounds).
+    uint32_t kmax = 0u, kmin = 0xffffffffu;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const bool valid = 64 * s + lane < Nb;
+      kmax = max(kmax, valid ? key[r][s] : 0u);
+      kmin = min(kmin, valid ? key[r][s] : 0xffffffffu);
+    }
+    for (int o = 32; o >= 1; o >>= 1) {
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+    }
+    kmax = __builtin_amdgcn_readfirstlane(kmax);
+    kmin = __builtin_amdgcn_readfirstlane(kmin);
+    const uint32_t diff = kmax ^ kmin;
+    const int top = diff ? 31 - __builtin_clz(diff) : -1;  // highest differing bit
+    // the shared prefix above `top` (all of kmax when every key is equal)
+    uint32_t T = top < 0 ? kmax : (top == 31 ? 0u : (kmax & ~((2u << top) - 1u)));
+    for (int b = top; b >= 0; --b) {
       const uint32_t cand = T | (1u << b);
       int cnt = 0;
 #pragma unroll
@@ -208,8 +227,12 @@ hipError_t launch_route(const Dims& dm, const Work& w, hipStream_t s) {
 #define PISA_ROUTE(D, NS, RPW)                                                             \
   hipLaunchKernelGGL((route_kernel<D, NS, RPW>), dim3((dm.Nb + 4 * RPW - 1) / (4 * RPW), dm.H), \
                      dim3(256), 0, s, dm, w)
-  if (dm.d == 128) {
-    if (ns <= 4) PISA_ROUTE(128, 4, 4);
+  if (dm.d == 128) {  // the tile count rounded up to an even number up to 12 (no idle tiles)
+    if (ns <= 2) PISA_ROUTE(128, 2, 4);
+    else if (ns <= 4) PISA_ROUTE(128, 4, 4);
+    else if (ns <= 6) PISA_ROUTE(128, 6, 4);
+    else if (ns <= 8) PISA_ROUTE(128, 8, 4);
+    else if (ns <= 10) PISA_ROUTE(128, 10, 4);
     else if (ns <= 12) PISA_ROUTE(128, 12, 4);
     else if (ns <= 16) PISA_ROUTE(128, 16, 4);
     else if (ns <= 32) PISA_ROUTE(128, 32, 2);
