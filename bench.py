@@ -115,8 +115,8 @@ def cpu_model() -> str:
     return platform.processor() or platform.machine()
 
 
-KERNELS = ("stats_pass_bf16", "stats_cov_bf16", "stats_finalize", "stats_f32", "route_kernel", "attend_bf16", "mfma_probe",
-           "attend_f32", "copyBuffer", "Fill")
+KERNELS = ("stats_qbar_bf16", "stats_pass_bf16", "stats_cov_chunk_bf16", "stats_cov_bf16", "stats_finalize", "stats_f32",
+           "route_kernel", "attend_bf16", "mfma_probe", "attend_f32", "copyBuffer", "Fill")
 
 
 def short_kernel(name: str) -> str:
@@ -170,7 +170,8 @@ def summarize_counters(d: str) -> None:
           "VALU / LDS / SALU / VMEM instr per MFMA | waves waiting (of wave time) | LDS bank conflicts "
           "(of LDS-active cycles) | L2 hit rate |")
     print("|---|---|---|---|---|---|---|---|")
-    for k in ("attend_bf16", "stats_pass_bf16", "stats_cov_bf16", "route_kernel", "stats_finalize", "mfma_probe"):
+    for k in ("attend_bf16", "stats_qbar_bf16", "stats_pass_bf16", "stats_cov_chunk_bf16", "stats_cov_bf16", "route_kernel",
+              "stats_finalize", "mfma_probe"):
         a = vals.get(k)
         if not a or not durs.get(k):
             continue
