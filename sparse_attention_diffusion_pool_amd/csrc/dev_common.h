@@ -98,20 +98,6 @@ __device__ __forceinline__ void tile_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t s
   }
 }
 
-// Same with the row count and wave count known at compile time (fully unrolled).
-template <bool TR, int ROWS, int NWAVES>
-__device__ __forceinline__ void tile_to_lds_n(__amdgpu_buffer_rsrc_t r, char* lds, int wave, int lane) {
-  static_assert(ROWS % (4 * NWAVES) == 0, "tile rows must split evenly over the waves");
-#pragma unroll
-  for (int m = 0; m < ROWS / 4 / NWAVES; ++m) {
-    const int n = m * NWAVES + wave;
-    const uint32_t row = 4 * n + (lane >> 4);
-    const uint32_t pos = lane & 15;
-    const uint32_t src_chunk = TR ? swz_tr(row, pos) : swz_row(row, pos);
-    buf_load_lds16(r, lds + 1024 * n, row * 256 + src_chunk * 16);
-  }
-}
-
 // Direct copy of a ROWS x 256 B tile by NWAVES waves, with the per-lane part of the global
 // offset precomputed (vbase = copy_vbase<TR>(wave, lane)); instruction m of wave w covers tile
 // rows 4 (m NWAVES + w) .. +3. The swizzle only depends on (row & 15), which is the same for every
@@ -214,11 +200,6 @@ __device__ __forceinline__ uint32_t copy_vbase(int wave, int lane, int extra_row
   const uint32_t pos = lane & 15;
   const uint32_t chunk = TR ? swz_tr(row, pos) : swz_row(row, pos);
   return row * 256 + chunk * 16;
-}
-
-// Address of a 16-byte row-read operand: row r, logical chunk c.
-__device__ __forceinline__ const char* row_addr(const char* tile, uint32_t r, uint32_t c) {
-  return tile + r * 256 + swz_row(r, c) * 16;
 }
 
 // Address for ds_read_b64_tr_b16 on a transpose-read tile: logical element (row r, column col),
