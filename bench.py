@@ -442,6 +442,90 @@ def latency_sweep(H, steps, warmup):
     return rows
 
 
+def power_trace(w, seconds: float = 4.0) -> None:
+    """Board power while the forward pass runs back to back, then while the MFMA probe loop runs
+    back to back (the same instruction with no data movement), each for about `seconds`. A thread
+    samples the amdgpu hwmon power reading (power1_input, else power1_average; microwatts) every
+    20 ms. Prints a markdown summary: mean and peak power per phase, the power cap, the forward's
+    time per call and the probe's rate and shader clock."""
+    import glob
+    import threading
+    import torch
+    from sparse_attention_diffusion_pool_amd import _lib as L
+    from workloads import layer_inputs
+
+    hw = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/"))
+    src = next((os.path.join(d, f) for d in hw for f in ("power1_input", "power1_average")
+                if os.path.exists(os.path.join(d, f))), None)
+    cap = next((os.path.join(d, "power1_cap") for d in hw if os.path.exists(os.path.join(d, "power1_cap"))), None)
+    if src is None:
+        print("no amdgpu hwmon power reading on this machine", file=sys.stderr)
+        sys.exit(1)
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        t0 = time.perf_counter()
+        while not stop.is_set():
+            try:
+                samples.append((time.perf_counter() - t0, float(open(src).read()) / 1e6))
+            except (OSError, ValueError):
+                pass
+            time.sleep(0.02)
+
+    q, k, v = layer_inputs(w)
+    dev = torch.device("cuda", 0)
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    plan = L.Plan(w.L, w.H, w.d, w.B, w.keep, dtype=L.DTYPE_BF16 if w.dtype == "bf16" else L.DTYPE_F32)
+    plan.attach_workspace(device=dev)
+    out = torch.empty_like(qd)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        plan.forward(qd, kd, vd, out, stream)
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    time.sleep(0.5)
+    marks = {}
+    t_start = time.perf_counter()
+    n_fwd = 0
+    marks["forward"] = [samples[-1][0] if samples else 0.0]
+    while time.perf_counter() - t_start < seconds:
+        for _ in range(10):
+            plan.forward(qd, kd, vd, out, stream)
+        n_fwd += 10
+        torch.cuda.synchronize()
+    fwd_ms = (time.perf_counter() - t_start) * 1e3 / n_fwd
+    marks["forward"].append(samples[-1][0])
+    time.sleep(1.0)
+    marks["probe"] = [samples[-1][0]]
+    t_start = time.perf_counter()
+    probes = []
+    while time.perf_counter() - t_start < seconds:
+        probes.append(mfma_probe(dev))
+    marks["probe"].append(samples[-1][0])
+    time.sleep(0.3)
+    stop.set()
+    th.join()
+    arr = np.array(samples)
+
+    def phase(a, b, trim=0.5):  # drop the ramp at the start of the phase
+        m = (arr[:, 0] >= a + trim) & (arr[:, 0] <= b)
+        return arr[m, 1]
+
+    fw, pr = phase(*marks["forward"]), phase(*marks["probe"])
+    idle = arr[arr[:, 0] < 0.45, 1]
+    cap_w = float(open(cap).read()) / 1e6 if cap else float("nan")
+    tf = float(np.mean([r["tflops"] for r in probes]))
+    ghz = float(np.mean([r["sclk_ghz"] for r in probes]))
+    print(f"{w.name}: power reading {src} (every 20 ms); cap {cap_w:.0f} W\n")
+    print("| phase | mean W | max W | samples | rate |")
+    print("|---|---|---|---|---|")
+    print(f"| idle (before) | {idle.mean():.0f} | {idle.max():.0f} | {len(idle)} | |")
+    print(f"| forward back to back | {fw.mean():.0f} | {fw.max():.0f} | {len(fw)} | {fwd_ms:.2f} ms per call |")
+    print(f"| MFMA probe back to back | {pr.mean():.0f} | {pr.max():.0f} | {len(pr)} | "
+          f"{tf:.0f} TFLOP/s at {ghz:.2f} GHz ({len(probes)} runs) |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -478,6 +562,9 @@ def main():
     ap.add_argument("--routing-quality", action="store_true",
                     help="compare routing variants (error vs dense, statistics + routing time) and exit")
     ap.add_argument("--sharpen", type=float, default=1.0, help="multiply Q by this factor (--routing-quality)")
+    ap.add_argument("--power-trace", action="store_true",
+                    help="board power while the forward pass runs back to back, then while the MFMA probe "
+                         "loop does (markdown table), and exit")
     args = ap.parse_args()
 
     if args.summarize_trace:
@@ -515,6 +602,10 @@ def main():
         return
     if args.sweep:
         latency_sweep(args.sweep_heads, args.steps, args.warmup)
+        return
+    if args.power_trace:
+        from workloads import workload
+        power_trace(workload(args.workload))
         return
     if args.routing_quality:
         from workloads import workload
