@@ -15,7 +15,8 @@ Modules:
 
 Pin status per function (what fixes it other than itself) is stated in each docstring;
 ``routing_scores(..., routing="cov")`` - the covariance-aware score formula - is a reading of
-the pages, not a printed formula, and is "parity unpinned" beyond the special cases listed there.
+the pages, not a printed formula: each of its terms is pinned by properties that fix it (listed in
+its docstring), while the choice of formula itself is "parity unpinned".
 """
 
 from . import brute, pisa_oracle  # noqa: F401

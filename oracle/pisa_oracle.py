@@ -127,8 +127,12 @@ def routing_scores(st: HeadStats, routing: str = "cov") -> np.ndarray:
     """Score_{i,j} for every (query block i, key block j), shape [Nb, Nb].
 
     "plain": qbar_i . kbar_j - pinned by the textbook top-k of the pooled product.
-    "cov":   qbar_i . kbar_j + ln(n_j + ||qbar_i||_2 M_j)  (R7, a reading: parity unpinned beyond
-             its special cases: with every M_j = 0 and full blocks it ranks like "plain").
+    "cov":   qbar_i . kbar_j + ln(n_j + ||qbar_i||_2 M_j)  (R7, a reading: the pages name the
+             ingredients, not the formula). Each term is pinned by properties that fix it: with
+             every M_j = 0 (constant keys per block, ragged last block) cov - plain = ln n_j; for
+             two blocks with equal centroids the score gap is ln((n + |qbar| M_0)/(n + |qbar| M_1))
+             with |qbar| and M_j formed outside the oracle; and |qbar (H_j - Hbar)| <= |qbar| M_j
+             (tests/test_oracle_pins.py). The choice of formula itself stays a reading.
     """
     base = st.qbar @ st.kbar.T
     if routing == "plain":
