@@ -183,7 +183,8 @@ __global__ __launch_bounds__(256, 2) void attend_bf16(Dims dm, Work w, const __b
   const bool do_tail = kk < Nb && (dm.phases & 2);
   const bool do_first = do_tail && (dm.phases & 4) && !dm.first_block;
   const bool block_fo = block_first_order(dm);  // per-block first order: finished by first_block_bf16
-  const int nc = do_tail ? dm.Nbp / BLK : 0;
+  // pooled steps: the kKT-token tiles that hold a pooled token j < N_b (tokens past N_b are zero)
+  const int nc = do_tail ? (Nb + kKT - 1) / kKT : 0;
   const __bf16* kl = reinterpret_cast<const __bf16*>(w.kbar_lo) + (size_t)h * dm.Nbp * 128;
   const __bf16* vl = reinterpret_cast<const __bf16*>(w.vbar_lo) + (size_t)h * dm.Nbp * 128;
   const __bf16* ht = reinterpret_cast<const __bf16*>(w.hbarT_lo) + (size_t)h * 128 * 128;
@@ -209,7 +210,7 @@ __global__ __launch_bounds__(256, 2) void attend_bf16(Dims dm, Work w, const __b
   const int rows_last = last_blk == Nb - 1 ? dm.n_last : B;
   const int E = (kk - 1) * SPB + (rows_last + kKT - 1) / kKT;  // exact steps
   const bool ragged = (rows_last % kKT) != 0;                   // last exact step is partial
-  const int S_main = E + nc * SPB;
+  const int S_main = E + nc;
   const int S_all = S_main + (do_first ? 1 : 0);
 
   // Byte offsets inside Q, K and V fit in 32 bits (the plan keeps H L d below 2^31 elements).
