@@ -4,9 +4,11 @@
 // "Covariance-aware routing" - the block first-order matrices H_j, their mean H-bar and
 // M_j = ||H_j - H-bar||).
 //
-// Pass A (one workgroup per 16 consecutive blocks of a head): column sums of Q, K, V per block
-// (pooled scaled query, key centroid, value sum) and the partial sum of the block first-order
-// matrices over its blocks, H_j = K_j^T V_j - kbar_j (sum V_j)^T (= sum_n (k_n - kbar_j)^T v_n).
+// Pass A (one workgroup per chunk of up to 16 consecutive blocks of a head): column sums of Q, K, V
+// per block (pooled scaled query, key centroid, value sum) and the partial sum of the block
+// first-order matrices over its blocks, H_j = K_j^T V_j - kbar_j (sum V_j)^T
+// (= sum_n (k_n - kbar_j)^T v_n). For bf16 inputs the Q column sums are a kernel of their own
+// (stats_qbar_bf16), so that pass A's loop moves only K and V.
 // Finalize (per head): H-bar = (sum of the partials) / N_b; bf16 copies of the pooled tokens and
 // of H-bar^T for the attention kernel. Covariance pass (one workgroup per chunk of blocks for the
 // Frobenius norm, one per block for the spectral norm and the H_j^T variant): H_j again, then
