@@ -53,3 +53,29 @@ def test_random_layer(seed):
         if nsel:
             log(f"[parity] random-{seed} head {h}: {nsel} rows differ by near-ties only")
     assert_close(pairs, res["dtype"], f"random-{seed}")
+
+
+# The routing kernel is instantiated per count of 64-key tiles (2, 4, 6, 8, 10, 12, 16, 32, 128).
+# The configurations reach 2, 4, 10 and 16, the large-N_b cases 32 and 128; these layers reach
+# the others: statistics and selection of every row, outputs on sampled query blocks.
+TILE_CASES = [  # (N_b, B)
+    (350, 128),   # 6 tiles
+    (449, 128),   # 8 tiles
+    (700, 128),   # 12 tiles
+    (330, 64),    # 6 tiles at B = 64
+]
+
+
+@pytest.mark.parametrize("nb,B", TILE_CASES, ids=[f"nb{nb}-B{B}" for nb, B in TILE_CASES])
+def test_routing_tile_counts(nb, B):
+    L = nb * B - 37  # ragged last block
+    w = custom(f"tiles-nb{nb}-B{B}", 1, (L,), 128, B, 0.1, "bf16", seed=900 + nb)
+    res = gpu_run(w, want_stats=True)
+    info = res["info"]
+    assert info["n_blocks"] == nb
+    rng = np.random.default_rng(nb)
+    qb = sorted(set(rng.choice(nb, size=6, replace=False).tolist()) | {nb - 1})
+    ref, out_ref, nsel = oracle_head(res, 0, query_blocks=qb)
+    check_stats(res, 0, ref)
+    log(f"[parity] tiles nb={nb} B={B}: k={info['k']}, {nsel} rows differ by near-ties only")
+    assert_close([compare_rows(res, 0, out_ref, qb, B)], res["dtype"], f"tiles nb={nb} B={B}")
