@@ -443,8 +443,9 @@ def latency_sweep(H, steps, warmup):
 
 
 def power_trace(w, seconds: float = 4.0) -> None:
-    """Board power while the forward pass runs back to back, then while the MFMA probe loop runs
-    back to back (the same instruction with no data movement), each for about `seconds`. A thread
+    """Board power while the forward pass runs back to back, then dense attention of the same layer
+    through the same kernel, then the MFMA probe loop (the same instruction with no data
+    movement), each for about `seconds`. A thread
     samples the amdgpu hwmon power reading (power1_input, else power1_average; microwatts) every
     20 ms. Prints a markdown summary: mean and peak power per phase, the power cap, the forward's
     time per call and the probe's rate and shader clock."""
@@ -497,6 +498,22 @@ def power_trace(w, seconds: float = 4.0) -> None:
     fwd_ms = (time.perf_counter() - t_start) * 1e3 / n_fwd
     marks["forward"].append(samples[-1][0])
     time.sleep(1.0)
+    # dense attention of the same layer through the same kernel (keep = 1, exact phase only)
+    dplan = L.Plan(w.L, w.H, w.d, w.B, 1.0, dtype=L.DTYPE_BF16 if w.dtype == "bf16" else L.DTYPE_F32, phases=1)
+    dplan.attach_workspace(device=dev)
+    dplan.forward(qd, kd, vd, out, stream)
+    torch.cuda.synchronize()
+    marks["dense"] = [samples[-1][0]]
+    t_start = time.perf_counter()
+    n_dense = 0
+    while time.perf_counter() - t_start < seconds:
+        dplan.forward_attend(qd, kd, vd, out, stream)
+        n_dense += 1
+        torch.cuda.synchronize()
+    dense_ms = (time.perf_counter() - t_start) * 1e3 / n_dense
+    marks["dense"].append(samples[-1][0])
+    dplan.destroy()
+    time.sleep(1.0)
     marks["probe"] = [samples[-1][0]]
     t_start = time.perf_counter()
     probes = []
@@ -512,7 +529,7 @@ def power_trace(w, seconds: float = 4.0) -> None:
         m = (arr[:, 0] >= a + trim) & (arr[:, 0] <= b)
         return arr[m, 1]
 
-    fw, pr = phase(*marks["forward"]), phase(*marks["probe"])
+    fw, dn, pr = phase(*marks["forward"]), phase(*marks["dense"]), phase(*marks["probe"])
     idle = arr[arr[:, 0] < 0.45, 1]
     cap_w = float(open(cap).read()) / 1e6 if cap else float("nan")
     tf = float(np.mean([r["tflops"] for r in probes]))
@@ -522,6 +539,8 @@ def power_trace(w, seconds: float = 4.0) -> None:
     print("|---|---|---|---|---|")
     print(f"| idle (before) | {idle.mean():.0f} | {idle.max():.0f} | {len(idle)} | |")
     print(f"| forward back to back | {fw.mean():.0f} | {fw.max():.0f} | {len(fw)} | {fwd_ms:.2f} ms per call |")
+    print(f"| dense attention (keep = 1) back to back | {dn.mean():.0f} | {dn.max():.0f} | {len(dn)} | "
+          f"{dense_ms:.1f} ms per call |")
     print(f"| MFMA probe back to back | {pr.mean():.0f} | {pr.max():.0f} | {len(pr)} | "
           f"{tf:.0f} TFLOP/s at {ghz:.2f} GHz ({len(probes)} runs) |")
 
@@ -563,8 +582,8 @@ def main():
                     help="compare routing variants (error vs dense, statistics + routing time) and exit")
     ap.add_argument("--sharpen", type=float, default=1.0, help="multiply Q by this factor (--routing-quality)")
     ap.add_argument("--power-trace", action="store_true",
-                    help="board power while the forward pass runs back to back, then while the MFMA probe "
-                         "loop does (markdown table), and exit")
+                    help="board power while the forward pass, dense attention through the same kernel and the "
+                         "MFMA probe loop each run back to back (markdown table), and exit")
     args = ap.parse_args()
 
     if args.summarize_trace:
