@@ -141,13 +141,26 @@ __device__ __forceinline__ uint32_t chunk_lane(int lane) {
 // results; their address operands are read when they issue. The row layout's other three offsets
 // are formed inside the block in scratch registers (kept out of the loop, they would hold three
 // registers for the whole kernel).
-template <bool TR>
+// NT (transpose-read tiles only) sets the non-temporal cache policy on the loads: for streams read
+// once per kernel, whose lines would only displace others from L2.
+template <bool TR, bool NT = false>
 __device__ __forceinline__ void copy_chunk_async(const u32x4& rsrc, uint32_t lds, uint32_t v0, uint32_t soff) {
+  static_assert(TR || !NT, "non-temporal copies are provided for transpose-read tiles");
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
   const u32x4 r = {(uint32_t)__builtin_amdgcn_readfirstlane(rsrc[0]), (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[1]),
                    (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[2]), (uint32_t)__builtin_amdgcn_readfirstlane(rsrc[3])};
   const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
-  if constexpr (TR) {
+  if constexpr (TR && NT) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen nt lds\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen offset:1024 nt lds\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen offset:2048 nt lds\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen offset:3072 nt lds"
+        :
+        : "s"(m0v), "v"(v0), "s"(r), "s"(so)
+        : "memory", "m0");
+  } else if constexpr (TR) {
     asm volatile(
         "s_mov_b32 m0, %0\n\ts_nop 0\n\t"
         "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
@@ -180,7 +193,7 @@ __device__ __forceinline__ void copy_chunk_async(const u32x4& rsrc, uint32_t lds
 // (zero bytes past them), so the rows past the end are zeros by the buffer range check on the
 // vector and instruction offsets alone: a raw buffer (stride 0) returns 0 for every load whose
 // offset lies at or beyond num_records (CDNA4 ISA, buffer instructions, range checking).
-template <int ROWS, int NWAVES, bool TR>
+template <int ROWS, int NWAVES, bool TR, bool NT = false>
 __device__ __forceinline__ void copy_tile_chunks(const void* base, uint32_t bytes, uint32_t lds, uint32_t v0,
                                                  int wave) {
   static_assert(ROWS % (16 * NWAVES) == 0, "tile rows must split into 16-row chunks over the waves");
@@ -188,8 +201,8 @@ __device__ __forceinline__ void copy_tile_chunks(const void* base, uint32_t byte
   for (int n = 0; n < ROWS / 16 / NWAVES; ++n) {
     const uint32_t c = n * NWAVES + wave;
     const uint32_t start = 4096u * c;
-    copy_chunk_async<TR>(rsrc_words(static_cast<const char*>(base) + start, bytes > start ? bytes - start : 0u),
-                         lds + start, v0, 0u);
+    copy_chunk_async<TR, NT>(rsrc_words(static_cast<const char*>(base) + start, bytes > start ? bytes - start : 0u),
+                             lds + start, v0, 0u);
   }
 }
 

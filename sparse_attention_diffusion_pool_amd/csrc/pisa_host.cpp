@@ -10,6 +10,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <new>
 #include <unordered_set>
@@ -65,11 +66,12 @@ Layout workspace_layout(const Dims& dm) {
   l.qbar = take(H * Nb * d * 4);
   l.kbar = take(H * Nb * d * 4);
   l.vsum = take(H * Nb * d * 4);
-  l.G = take(H * (size_t)dm.NC * d * d * 4);
+  const size_t slots = dm.dtype == PISA_DTYPE_BF16 ? (size_t)pisa::stat_slots(dm) : H * (size_t)dm.NC;
+  l.G = take(slots * d * d * 4);
   l.hbar = take(H * d * d * 4);
   l.M = take(H * Nb * 4);
   if (dm.dtype == PISA_DTYPE_BF16) {
-    l.kpart = take(H * (size_t)dm.NC * d * 4);
+    l.kpart = take(slots * d * 4);
     l.kc = take(H * d * 4);
     l.kbar_lo = take(H * (size_t)dm.Nbp * d * 2);
     l.vbar_lo = take(H * (size_t)dm.Nbp * d * 2);
@@ -148,6 +150,11 @@ void derive(pisa::Dims& dm, double keep) {
   dm.chunk = pisa::kStatsChunk;
   while (dm.chunk > 4 && (long long)((dm.Nb + dm.chunk - 1) / dm.chunk) * dm.H < 512) dm.chunk /= 2;
   dm.NC = (dm.Nb + dm.chunk - 1) / dm.chunk;
+  // bf16 statistics passes: one range of (head, block) pairs per workgroup, two workgroups per CU
+  // on a 256-CU chip, and at least about 4 blocks per range so that each partial sum written
+  // (64 KB) stands for several blocks
+  const long long pairs = (long long)dm.H * dm.Nb;
+  dm.SW = (int)std::min<long long>(pisa::kStatsWorkgroups, std::max<long long>(1, (pairs + 3) / 4));
   dm.Nbp = ((dm.Nb + dm.B - 1) / dm.B) * dm.B;
 }
 

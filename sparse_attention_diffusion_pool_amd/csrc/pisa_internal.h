@@ -10,6 +10,8 @@ namespace pisa {
 // Most blocks whose K^T V products one statistics workgroup sums before writing a partial of
 // H-bar (Dims::chunk is this, or less for layers too small to fill the chip with 16).
 constexpr int kStatsChunk = 16;
+// Most workgroups of the bf16 statistics passes (two resident per CU on 256 CUs: one round).
+constexpr int kStatsWorkgroups = 512;
 
 struct Dims {
   int H;
@@ -27,8 +29,25 @@ struct Dims {
   int dtype;   // 0 bf16, 1 fp32
   int first_block;  // 1: block-wise first-order term (per-block H_j) instead of H-bar
   int spectral;     // 1: M_j = spectral norm of H_j - H-bar (default Frobenius)
-  int chunk;        // blocks per statistics workgroup (<= kStatsChunk)
+  int chunk;        // blocks per statistics workgroup (<= kStatsChunk; fp32 and per-block passes)
+  int SW;           // workgroups of the bf16 statistics and Frobenius covariance passes
 };
+
+// The bf16 statistics and Frobenius covariance passes split the H * N_b (head, block) pairs, taken
+// in head-major order g = h * N_b + j, into SW contiguous ranges whose lengths differ by at most one:
+// range w is [stat_range_begin(w), stat_range_begin(w + 1)). A range may meet several heads; its
+// partial sums for head h go to slot w + h. No two (range, head) pairs share a slot: a later range
+// w' > w meets no head before the last head range w meets, so w' + h' > w + h. Head h's partials
+// are the slots stat_owner(h N_b) + h .. stat_owner(h N_b + N_b - 1) + h.
+__host__ __device__ inline int stat_range_begin(const Dims& dm, int w) {
+  return (int)(((long long)w * dm.H * dm.Nb) / dm.SW);
+}
+// The range holding pair g (every range holds at least one pair: SW <= H * N_b).
+__host__ __device__ inline int stat_owner(const Dims& dm, int g) {
+  return (int)((((long long)g + 1) * dm.SW - 1) / ((long long)dm.H * dm.Nb));
+}
+// Partial slots of the bf16 statistics pass: at most SW + H - 1.
+__host__ __device__ inline int stat_slots(const Dims& dm) { return dm.SW + dm.H - 1; }
 
 // The block-wise first-order variant runs when it is requested and there is a first-order term.
 __host__ __device__ inline bool block_first_order(const Dims& dm) {
@@ -40,10 +59,11 @@ struct Work {
   float* qbar;      // [H][Nb][d]   pooled scaled queries (mean of scale*q over the block)
   float* kbar;      // [H][Nb][d]   key centroids
   float* vsum;      // [H][Nb][d]   value sums
-  float* G;         // [H][NC][d][d] partial sums of H_j = K_j^T V_j - kbar_j (sum V_j)^T
+  float* G;         // [slots][d][d] partial sums of H_j = K_j^T V_j - kbar_j (sum V_j)^T: fp32 path
+                    // H * NC slots (slot h NC + c), bf16 path stat_slots (slot w + h)
   float* hbar;      // [H][d][d]    H-bar
   float* M;         // [H][Nb]      ||H_j - H-bar||_F
-  float* kpart;     // [H][NC][d]   per-chunk sums of the block centroids    (bf16 path only)
+  float* kpart;     // [slots][d]   partial sums of the block centroids, slots as G (bf16 path only)
   float* kc;        // [H][d]       key centre: mean of the block centroids   (bf16 path only)
   void* kbar_lo;    // bf16 [H][Nbp][d] centroid minus the key centre, zero rows past Nb (bf16 path only)
   void* vbar_lo;    // bf16 [H][Nbp][d] value means, zero rows past Nb    (bf16 path only)

@@ -4,14 +4,16 @@
 // "Covariance-aware routing" - the block first-order matrices H_j, their mean H-bar and
 // M_j = ||H_j - H-bar||).
 //
-// Pass A (one workgroup per chunk of up to 16 consecutive blocks of a head): column sums of Q, K, V
-// per block (pooled scaled query, key centroid, value sum) and the partial sum of the block
-// first-order matrices over its blocks, H_j = K_j^T V_j - kbar_j (sum V_j)^T
-// (= sum_n (k_n - kbar_j)^T v_n). For bf16 inputs the Q column sums are a kernel of their own
-// (stats_qbar_bf16), so that pass A's loop moves only K and V.
+// Pass A: column sums of Q, K, V per block (pooled scaled query, key centroid, value sum) and
+// partial sums of the block first-order matrices H_j = K_j^T V_j - kbar_j (sum V_j)^T
+// (= sum_n (k_n - kbar_j)^T v_n). fp32 inputs: one workgroup per chunk of up to 16 consecutive
+// blocks of a head. bf16 inputs: one workgroup per range of consecutive (head, block) pairs, the
+// ranges of equal length over all heads (one round of workgroups on the chip, one partial per head
+// a range meets); the Q column sums are a kernel of their own (stats_qbar_bf16), so that pass A's
+// loop moves only K and V.
 // Finalize (per head): H-bar = (sum of the partials) / N_b; bf16 copies of the pooled tokens and
-// of H-bar^T for the attention kernel. Covariance pass (one workgroup per chunk of blocks for the
-// Frobenius norm, one per block for the spectral norm and the H_j^T variant): H_j again, then
+// of H-bar^T for the attention kernel. Covariance pass (bf16 Frobenius norm: the statistics pass's
+// ranges; fp32, the spectral norm and the H_j^T variant: one workgroup per block): H_j again, then
 // M_j = ||H_j - H-bar|| (and H_j^T in bf16 for the block-wise first-order variant).
 //
 // bf16 inputs: K_j^T V_j on v_mfma_f32_32x32x16_bf16 (products of bf16 values are exact in fp32,
@@ -90,7 +92,8 @@ __global__ __launch_bounds__(256) void stats_qbar_bf16(Dims dm, Work w, const __
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + r0, n * 256);
   u32x4 qa[QR];
 #pragma unroll
-  for (int e = 0; e < QR; ++e) qa[e] = buf_load16(rq, (rg + 16 * e) * 256 + p * 16);
+  for (int e = 0; e < QR; ++e)  // read once: non-temporal (cache policy bit 1)
+    qa[e] = __builtin_amdgcn_raw_buffer_load_b128(rq, (rg + 16 * e) * 256 + p * 16, 0, 2);
   float qs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int e = 0; e < QR; ++e) {
@@ -118,6 +121,9 @@ __global__ __launch_bounds__(256) void stats_qbar_bf16(Dims dm, Work w, const __
 // as for the whole block; rows of a half past the block end are written as zeros (each 16-row
 // chunk's buffer resource ends where the block's rows end).
 //
+// Each pass reads every K and V byte once: the copies carry the non-temporal hint, so that the two
+// streams do not displace other lines (the passes' own output rows among them) from L2.
+//
 // The copies are issued from assembly (copy_tile_chunks), out of sight of the compiler's
 // wait-count insertion, which cannot tell copies into one slot from reads of the other and would
 // make every read wait for the latest copy. The loops issue no other global loads, so the waits
@@ -130,12 +136,12 @@ __device__ __forceinline__ void kv_half_copy(const __bf16* K, const __bf16* V, s
   const __bf16* kb = K + r0 + (size_t)HR * half * 128;
   const __bf16* vb = V + r0 + (size_t)HR * half * 128;
   if constexpr (HR % 64 == 0) {  // every wave copies a chunk of K and one of V
-    copy_tile_chunks<HR, 4, true>(kb, bytes, kslot, v0, wave);
-    copy_tile_chunks<HR, 4, true>(vb, bytes, vslot, v0, wave);
+    copy_tile_chunks<HR, 4, true, true>(kb, bytes, kslot, v0, wave);
+    copy_tile_chunks<HR, 4, true, true>(vb, bytes, vslot, v0, wave);
   } else {  // 32-row halves: waves 0-1 copy K's two chunks, waves 2-3 V's
     static_assert(HR == 32, "half-block rows");
-    if (wave < 2) copy_tile_chunks<HR, 2, true>(kb, bytes, kslot, v0, wave);
-    else copy_tile_chunks<HR, 2, true>(vb, bytes, vslot, v0, wave - 2);
+    if (wave < 2) copy_tile_chunks<HR, 2, true, true>(kb, bytes, kslot, v0, wave);
+    else copy_tile_chunks<HR, 2, true, true>(vb, bytes, vslot, v0, wave - 2);
   }
 }
 
@@ -160,10 +166,12 @@ __device__ __forceinline__ void wait_vmem_but() {
   __asm__ __volatile__("" ::: "memory");
 }
 
-// Pass A, bf16: column sums of K and V and K^T V (matrix unit, from LDS) over the chunk's blocks,
-// through the half-block ring. The chunk's partial is corrected by the centroids block by block:
-// G_c = sum_{j in c} (K_j^T V_j - kbar_j (sum V_j)^T) = sum_{j in c} H_j. The Q column sums are
-// stats_qbar_bf16's.
+// Pass A, bf16: column sums of K and V and K^T V (matrix unit, from LDS) over the workgroup's range
+// of (head, block) pairs, through the half-block ring, which runs on across head boundaries. For each
+// head the range meets, the partial is corrected by the centroids block by block,
+// G = sum_j (K_j^T V_j - kbar_j (sum V_j)^T) = sum_j H_j over the range's blocks of that head, and
+// written with the centroids' partial sum to the head's slot when the range leaves the head. The Q
+// column sums are stats_qbar_bf16's.
 template <int BLK>
 __global__ __launch_bounds__(256, 2) void stats_pass_bf16(Dims dm, Work w, const __bf16* __restrict__ K,
                                                           const __bf16* __restrict__ V) {
@@ -171,93 +179,115 @@ __global__ __launch_bounds__(256, 2) void stats_pass_bf16(Dims dm, Work w, const
   __shared__ __attribute__((aligned(1024))) char Ks1[BLK * 128];
   __shared__ __attribute__((aligned(1024))) char Vs0[BLK * 128];
   __shared__ __attribute__((aligned(1024))) char Vs1[BLK * 128];
-  __shared__ float svs[128];  // the current block's value sums
-  __shared__ float kcs[128];  // the chunk's sum of block centroids (row a owned by one lane)
+  // centroids and value sums of a group of up to kStage consecutive blocks, stored together
+  constexpr int kStage = 8;
+  __shared__ __attribute__((aligned(16))) float stk[kStage * 128];
+  __shared__ __attribute__((aligned(16))) float stv[kStage * 128];
   constexpr int HR = BLK / 2;
   constexpr int NV = kv_half_vmem<BLK>();
-  const int h = blockIdx.y, c = blockIdx.x;
+  const int wg = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int j0 = c * dm.chunk, j1 = min(dm.Nb, j0 + dm.chunk);
-  const size_t head = (size_t)h * dm.L * 128;
+  const int g0 = stat_range_begin(dm, wg), g1 = stat_range_begin(dm, wg + 1);
   const uint32_t hh = lane >> 5, l32 = lane & 31;
   const uint32_t v0 = chunk_lane<true>(lane);
   const uint32_t k0 = lds_addr(Ks0), k1 = lds_addr(Ks1), s0 = lds_addr(Vs0), s1 = lds_addr(Vs1);
   f32x16 acc[4];
   for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x16{};
-  if (tid < 128) kcs[tid] = 0.f;  // first read after the first block's barriers
+  // the head's sum of block centroids over the range so far; every lane holds the rows of its
+  // accumulator entries (a = 32 wave + 8 (x >> 2) + 4 hh + (x & 3)), lanes l32 = 0 write them
+  float kc[16];
+#pragma unroll
+  for (int x = 0; x < 16; ++x) kc[x] = 0.f;
 
   auto rows_of = [&](int j) { return (j == dm.Nb - 1) ? dm.n_last : dm.B; };
-  auto issue = [&](int j, int half) __attribute__((always_inline)) {
-    kv_half_copy<BLK>(K, V, head + (size_t)j * dm.B * 128, rows_of(j), half, half ? k1 : k0, half ? s1 : s0, v0,
-                      wave);
+  auto issue = [&](int g, int half) __attribute__((always_inline)) {
+    const int h = g / dm.Nb, j = g - h * dm.Nb;
+    kv_half_copy<BLK>(K, V, (size_t)h * dm.L * 128 + (size_t)j * dm.B * 128, rows_of(j), half, half ? k1 : k0,
+                      half ? s1 : s0, v0, wave);
   };
-  // a block's outputs are stored after the next block's first barrier (or after the loop): the
-  // copies then stay the most recent vector-memory operations at every wait
-  float pk[16], pv = 0.f;
-  size_t pob = 0;
-  auto store_pending = [&]() __attribute__((always_inline)) {
-    if (l32 == 0) {
-#pragma unroll
-      for (int x = 0; x < 16; ++x) w.kbar[pob + 32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3)] = pk[x];
+  // A store issued inside the ring counts against the copies' wait that follows it: a group's
+  // outputs are therefore stored at once, after the first barrier of the block that follows the
+  // group (or after the loop), one 16-byte piece per thread and array: pairs pg .. pg + cnt - 1 are
+  // consecutive rows of kbar and vsum.
+  auto store_group = [&](int pg, int cnt) __attribute__((always_inline)) {
+    if (4 * tid < cnt * 128) {
+      *reinterpret_cast<float4*>(w.kbar + (size_t)pg * 128 + 4 * tid) = *reinterpret_cast<const float4*>(stk + 4 * tid);
+      *reinterpret_cast<float4*>(w.vsum + (size_t)pg * 128 + 4 * tid) = *reinterpret_cast<const float4*>(stv + 4 * tid);
     }
-    if (lane < 32) w.vsum[pob + 32 * wave + lane] = pv;
   };
-  if (j0 < j1) {
-    issue(j0, 0);
-    issue(j0, 1);
+  if (g0 < g1) {
+    issue(g0, 0);
+    issue(g0, 1);
   }
-  for (int j = j0; j < j1; ++j) {
+  for (int g = g0; g < g1; ++g) {
+    const int h = g / dm.Nb, j = g - h * dm.Nb;
     const int n = rows_of(j);
-    const bool more = j + 1 < j1;
+    const bool more = g + 1 < g1;
+    const int sl = (g - g0) % kStage;  // the block's row in the group's staging arrays
     f32x16 ksum = f32x16{}, vsum = f32x16{};
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      // half (j, half) landed; the half issued after it, if any, stays in flight
+      // half (g, half) landed; the half issued after it, if any, stays in flight. Loads complete
+      // in issue order, so stores issued between the copies do not weaken the count.
       if (half == 0 || more) wait_vmem_but<NV>(); else wait_vmem();
       lds_barrier();
-      if (half == 0 && j > j0) store_pending();
+      if (half == 0 && g > g0 && sl == 0) store_group(g - kStage, kStage);
       ktv_mfma_sums<HR>(half ? Ks1 : Ks0, half ? Vs1 : Vs0, acc, ksum, vsum, wave, lane);
       lds_barrier();  // every wave done with this half's slots
-      if (more) issue(j + 1, half);
+      if (more) issue(g + 1, half);
     }
     const float inv = 1.0f / (float)n;
-    pob = ((size_t)h * dm.Nb + j) * 128;
     // lane l's ksum[x] is the column sum of K for row a = 32 wave + 8 (x >> 2) + 4 hh + (x & 3) of
     // the product, the same row as acc[.][x]
+    float pk[16];
 #pragma unroll
-    for (int x = 0; x < 16; ++x) pk[x] = ksum[x] * inv;
-    if (l32 == 0) {
-#pragma unroll
-      for (int x = 0; x < 16; ++x) kcs[32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3)] += pk[x];
+    for (int x = 0; x < 16; ++x) {
+      pk[x] = ksum[x] * inv;
+      kc[x] += pk[x];
     }
-    pv = vsum[0];
-    if (lane < 32) svs[32 * wave + lane] = pv;
-    lds_barrier();  // svs complete (next written after the next block's first barrier)
+    float* rk = stk + sl * 128;
+    float* rv = stv + sl * 128;
+    if (l32 == 0) {  // rows 32 wave + 8 q + 4 hh + (0..3): four consecutive floats per q
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(rk + 32 * wave + 8 * q + 4 * hh) =
+            make_float4(pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]);
+    }
+    if (lane < 32) rv[32 * wave + lane] = vsum[0];
+    lds_barrier();  // the block's row complete (the row is next written kStage blocks on)
     // acc[ct][x] -= kbar_j[a] vsum_j[b], b = 32 ct + l32
     float vb[4];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) vb[ct] = svs[32 * ct + l32];
+    for (int ct = 0; ct < 4; ++ct) vb[ct] = rv[32 * ct + l32];
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) acc[ct][x] = fmaf(-pk[x], vb[ct], acc[ct][x]);
     }
-  }
-  if (j0 < j1) store_pending();
-  float* G = w.G + ((size_t)h * dm.NC + c) * 128 * 128;
-  for (int ct = 0; ct < 4; ++ct)
-    for (int x = 0; x < 16; ++x) {
-      const int a = 32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3);
-      G[a * 128 + 32 * ct + l32] = acc[ct][x];
-    }
-  if (l32 == 0) {  // each row a was summed by this lane alone
-    float* kp = w.kpart + ((size_t)h * dm.NC + c) * 128;
+    if (!more || j == dm.Nb - 1) {  // the range leaves head h: its partials go to slot wg + h
+      const size_t slot = (size_t)wg + h;
+      float* G = w.G + slot * 128 * 128;
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const int a = 32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3);
-      kp[a] = kcs[a];
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          const int a = 32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3);
+          G[a * 128 + 32 * ct + l32] = acc[ct][x];
+          acc[ct][x] = 0.f;
+        }
+      if (l32 == 0) {
+        float* kp = w.kpart + slot * 128;
+#pragma unroll
+        for (int x = 0; x < 16; ++x) kp[32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3)] = kc[x];
+      }
+#pragma unroll
+      for (int x = 0; x < 16; ++x) kc[x] = 0.f;
     }
+  }
+  if (g0 < g1) {
+    const int cnt = (g1 - 1 - g0) % kStage + 1;
+    store_group(g1 - cnt, cnt);
   }
 }
 
@@ -473,11 +503,11 @@ __global__ __launch_bounds__(256) void stats_cov_bf16(Dims dm, Work w, const __b
   if (tid == 0) w.M[(size_t)h * dm.Nb + j] = sqrtf(red[0] + red[1] + red[2] + red[3]);
 }
 
-// Covariance pass, Frobenius M_j (the default): one workgroup per chunk of dm.chunk blocks, like the
-// statistics pass and through the same half-block ring, with the lane's 64 entries of H-bar held in
-// registers for the whole chunk. The block's centroid and value sums are formed again on the
-// matrix unit beside K^T V (the same instructions in the same order as the statistics pass, so the
-// same values) rather than read back: the loop then issues no global loads besides the copies.
+// Covariance pass, Frobenius M_j (the default): one workgroup per range of (head, block) pairs, the
+// statistics pass's ranges, through the same half-block ring, with the lane's 64 entries of H-bar
+// held in registers (loaded again when the range enters another head). The block's centroid and value sums are formed again on the matrix unit beside K^T V
+// (the same instructions in the same order as the statistics pass, so the same values) rather
+// than read back: the loop then issues no global loads besides the copies and the H-bar rows.
 template <int BLK>
 __global__ __launch_bounds__(256, 2) void stats_cov_chunk_bf16(Dims dm, Work w, const __bf16* __restrict__ K,
                                                                const __bf16* __restrict__ V) {
@@ -487,62 +517,79 @@ __global__ __launch_bounds__(256, 2) void stats_cov_chunk_bf16(Dims dm, Work w, 
   __shared__ __attribute__((aligned(1024))) char Vs1[BLK * 128];
   __shared__ float svs[2][128];  // value sums of the block (alternating buffers)
   __shared__ float red[2][4];
+  // M of a group of up to kStage consecutive blocks, stored together: a store issued inside the
+  // ring counts against the copies' wait that follows it
+  constexpr int kStage = 8;
+  __shared__ float sM[kStage];
   constexpr int HR = BLK / 2;
   constexpr int NV = kv_half_vmem<BLK>();
-  const int h = blockIdx.y, c = blockIdx.x;
+  const int wg = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, l32 = lane & 31;
-  const int j0 = c * dm.chunk, j1 = min(dm.Nb, j0 + dm.chunk);
-  const size_t head = (size_t)h * dm.L * 128;
+  const int g0 = stat_range_begin(dm, wg), g1 = stat_range_begin(dm, wg + 1);
   const uint32_t v0 = chunk_lane<true>(lane);
   const uint32_t k0 = lds_addr(Ks0), k1 = lds_addr(Ks1), s0 = lds_addr(Vs0), s1 = lds_addr(Vs1);
   auto rows_of = [&](int j) { return (j == dm.Nb - 1) ? dm.n_last : dm.B; };
-  auto issue = [&](int j, int half) __attribute__((always_inline)) {
-    kv_half_copy<BLK>(K, V, head + (size_t)j * dm.B * 128, rows_of(j), half, half ? k1 : k0, half ? s1 : s0, v0,
-                      wave);
+  auto issue = [&](int g, int half) __attribute__((always_inline)) {
+    const int h = g / dm.Nb, j = g - h * dm.Nb;
+    kv_half_copy<BLK>(K, V, (size_t)h * dm.L * 128 + (size_t)j * dm.B * 128, rows_of(j), half, half ? k1 : k0,
+                      half ? s1 : s0, v0, wave);
   };
-  if (j0 < j1) {
-    issue(j0, 0);
-    issue(j0, 1);
+  auto m_of = [&](int t) { return sqrtf(red[t & 1][0] + red[t & 1][1] + red[t & 1][2] + red[t & 1][3]); };
+  if (g0 < g1) {
+    issue(g0, 0);
+    issue(g0, 1);
   }
-  const float* hb = w.hbar + (size_t)h * 128 * 128;
   float hbr[4][16];  // H-bar[a][b] for the lane's accumulator entries (a, b as in acc[ct][x])
+  int hcur = -1;
+  for (int t = 0; t < g1 - g0; ++t) {
+    const int g = g0 + t;
+    const int h = g / dm.Nb, j = g - h * dm.Nb;
+    const bool more = g + 1 < g1;
+    const bool fresh = h != hcur;
+    if (fresh) {
+      // through a buffer resource: one lane offset, the entry's offset an immediate or a scalar
+      const __amdgpu_buffer_rsrc_t rh = make_rsrc(w.hbar + (size_t)h * 128 * 128, 128 * 128 * 4);
+      const uint32_t lo = 4u * ((32 * wave + 4 * hh) * 128 + l32);
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
+      for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-    for (int x = 0; x < 16; ++x)
-      hbr[ct][x] = hb[(32 * wave + 8 * (x >> 2) + 4 * hh + (x & 3)) * 128 + 32 * ct + l32];
-  for (int j = j0; j < j1; ++j) {
-    const bool more = j + 1 < j1;
+        for (int x = 0; x < 16; ++x)
+          hbr[ct][x] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              rh, lo, 4 * ((8 * (x >> 2) + (x & 3)) * 128 + 32 * ct), 0));
+      // wait for everything (the copies in flight too): the rows are then complete, and the
+      // compiler, which does not count the copies, knows it and inserts no wait of its own later
+      wait_vmem();
+      hcur = h;
+    }
     f32x16 acc[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x16{};
     f32x16 ksum = f32x16{}, vsum = f32x16{};
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      // half (j, half) landed; the half issued after it, if any, stays in flight (the stores
-      // issued since are younger still). The first block waits for everything: the H-bar loads
-      // above are then complete, and the compiler, which does not count the copies, inserts no
-      // wait of its own for them later.
-      if (half == 0 && j == j0) wait_vmem();
-      else if (half == 0 || more) wait_vmem_but<NV>();
-      else wait_vmem();
+      // half (g, half) landed; the half issued after it, if any, stays in flight (the stores
+      // issued since are younger still)
+      if (half == 0 || more) wait_vmem_but<NV>(); else wait_vmem();
       lds_barrier();
-      if (half == 0 && j > j0 && tid == 0)  // M of the previous block (partials written before the barrier)
-        w.M[(size_t)h * dm.Nb + j - 1] =
-            sqrtf(red[(j - 1) & 1][0] + red[(j - 1) & 1][1] + red[(j - 1) & 1][2] + red[(j - 1) & 1][3]);
+      if (half == 0 && t > 0) {  // M of the previous block (pair g - 1)
+        if (tid == 0) sM[(t - 1) % kStage] = m_of(t - 1);
+        // a complete group, pairs g - kStage .. g - 1, by wave 0 (which wrote sM; its LDS accesses
+        // are done in order)
+        if ((t - 1) % kStage == kStage - 1 && tid < kStage) w.M[g - kStage + tid] = sM[tid];
+      }
       ktv_mfma_sums<HR>(half ? Ks1 : Ks0, half ? Vs1 : Vs0, acc, ksum, vsum, wave, lane);
       lds_barrier();  // every wave done with this half's slots
-      if (more) issue(j + 1, half);
+      if (more) issue(g + 1, half);
     }
     const float inv = 1.0f / (float)rows_of(j);
-    if (lane < 32) svs[j & 1][32 * wave + lane] = vsum[0];
-    lds_barrier();  // svs[j & 1] complete; it is next written two blocks on, after several barriers
+    if (lane < 32) svs[t & 1][32 * wave + lane] = vsum[0];
+    lds_barrier();  // svs[t & 1] complete; it is next written two blocks on, after several barriers
     float ss = 0.f;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      const float vb = svs[j & 1][32 * ct + l32];
+      const float vb = svs[t & 1][32 * ct + l32];
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         const float hv = fmaf(-(ksum[x] * inv), vb, acc[ct][x]) - hbr[ct][x];
@@ -550,13 +597,13 @@ __global__ __launch_bounds__(256, 2) void stats_cov_chunk_bf16(Dims dm, Work w, 
       }
     }
     ss = wave_sum(ss);
-    if (lane == 0) red[j & 1][wave] = ss;  // read after the next block's first barrier
+    if (lane == 0) red[t & 1][wave] = ss;  // read after the next block's first barrier
   }
-  if (j0 < j1) {
+  if (g0 < g1) {  // the last block's M, then the last group (pairs g1 - cnt .. g1 - 1)
     lds_barrier();
-    if (tid == 0)
-      w.M[(size_t)h * dm.Nb + j1 - 1] =
-          sqrtf(red[(j1 - 1) & 1][0] + red[(j1 - 1) & 1][1] + red[(j1 - 1) & 1][2] + red[(j1 - 1) & 1][3]);
+    const int n = g1 - g0, cnt = (n - 1) % kStage + 1;
+    if (tid == 0) sM[(n - 1) % kStage] = m_of(n - 1);
+    if (tid < cnt) w.M[g1 - cnt + tid] = sM[tid];
   }
 }
 
@@ -659,8 +706,8 @@ __global__ __launch_bounds__(256) void stats_f32(Dims dm, Work w, const float* _
 }
 
 // ---------------------------------------------------------------------------------------------
-// Finalize: H-bar = (sum_c G_c) / N_b (the partials already hold sum_{j in c} H_j), and (bf16 path)
-// bf16 pooled tokens and H-bar^T. Grid (D * D / 256, H): one H-bar entry per thread; pooled rows
+// Finalize: H-bar = (sum of the head's partials G) / N_b (each partial already holds the sum of H_j
+// over its blocks, summed here in slot order), and (bf16 path) bf16 pooled tokens and H-bar^T. Grid (D * D / 256, H): one H-bar entry per thread; pooled rows
 // are spread over the same grid.
 // ---------------------------------------------------------------------------------------------
 
@@ -669,14 +716,18 @@ __global__ __launch_bounds__(256) void stats_finalize(Dims dm, Work w) {
   const int h = blockIdx.y, x = blockIdx.x, tid = threadIdx.x;
   const int e = x * 256 + tid;  // entry a * D + b
   const int a = e / D, b = e % D;
-  const float* G = w.G + (size_t)h * dm.NC * D * D + e;
-  // bf16 path: the chunk sums of the block centroids (column tid % D) are added in the same loop,
-  // so their loads are in flight together with the partials of H-bar
+  // the head's partial slots: fp32 path h NC .. h NC + NC - 1, bf16 path those of the ranges that
+  // meet head h
   const bool cen = dm.dtype == 0;
-  const float* kp = cen ? w.kpart + (size_t)h * dm.NC * D + (tid % D) : G;
+  const int p0 = cen ? stat_owner(dm, h * dm.Nb) + h : h * dm.NC;
+  const int np = cen ? stat_owner(dm, h * dm.Nb + dm.Nb - 1) + h + 1 - p0 : dm.NC;
+  const float* G = w.G + (size_t)p0 * D * D + e;
+  // bf16 path: the partial sums of the block centroids (column tid % D) are added in the same
+  // loop, so their loads are in flight together with the partials of H-bar
+  const float* kp = cen ? w.kpart + (size_t)p0 * D + (tid % D) : G;
   float g0 = 0.f, g1 = 0.f, g2 = 0.f, g3 = 0.f, k0 = 0.f, k1 = 0.f, k2 = 0.f, k3 = 0.f;
   int c = 0;
-  for (; c + 4 <= dm.NC; c += 4) {
+  for (; c + 4 <= np; c += 4) {
     g0 += G[(size_t)c * D * D];
     g1 += G[(size_t)(c + 1) * D * D];
     g2 += G[(size_t)(c + 2) * D * D];
@@ -688,7 +739,7 @@ __global__ __launch_bounds__(256) void stats_finalize(Dims dm, Work w) {
       k3 += kp[(size_t)(c + 3) * D];
     }
   }
-  for (; c < dm.NC; ++c) {
+  for (; c < np; ++c) {
     g0 += G[(size_t)c * D * D];
     if (cen) k0 += kp[(size_t)c * D];
   }
@@ -724,7 +775,7 @@ __global__ __launch_bounds__(256) void stats_finalize(Dims dm, Work w) {
 
 hipError_t launch_stats_pass_bf16(const Dims& dm, const Work& w, const void* Q, const void* K, const void* V,
                                   hipStream_t s) {
-  dim3 grid(dm.NC, dm.H), qgrid(dm.Nb, dm.H);
+  dim3 grid(dm.SW), qgrid(dm.Nb, dm.H);
   auto q = static_cast<const __bf16*>(Q);
   auto k = static_cast<const __bf16*>(K);
   auto v = static_cast<const __bf16*>(V);
@@ -746,7 +797,7 @@ hipError_t launch_stats_cov_bf16(const Dims& dm, const Work& w, const void* K, c
   hipLaunchKernelGGL((stats_cov_bf16<BLK, SPEC, HJT>), grid, dim3(256), 0, s, dm, w, k, v)
   const bool hjt = block_first_order(dm);
   if (!dm.spectral && !hjt) {
-    dim3 cgrid(dm.NC, dm.H);
+    dim3 cgrid(dm.SW);
     if (dm.B == 128)
       hipLaunchKernelGGL(stats_cov_chunk_bf16<128>, cgrid, dim3(256), 0, s, dm, w, k, v);
     else

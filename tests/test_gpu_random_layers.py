@@ -79,3 +79,25 @@ def test_routing_tile_counts(nb, B):
     check_stats(res, 0, ref)
     log(f"[parity] tiles nb={nb} B={B}: k={info['k']}, {nsel} rows differ by near-ties only")
     assert_close([compare_rows(res, 0, out_ref, qb, B)], res["dtype"], f"tiles nb={nb} B={B}")
+
+
+# The bf16 statistics passes give each workgroup a range of about four consecutive (head, block)
+# pairs on layers this small, so with one, two or six blocks per head a range meets two, three or
+# four heads, and its partial sums of H-bar and of the centroids go to one slot per head met.
+MANY_HEADS = [  # (H, L, B)
+    (7, 100, 128),   # N_b = 1
+    (5, 200, 128),   # N_b = 2
+    (9, 330, 64),    # N_b = 6
+]
+
+
+@pytest.mark.parametrize("H,L,B", MANY_HEADS, ids=[f"H{H}-L{L}-B{B}" for H, L, B in MANY_HEADS])
+def test_ranges_across_heads(H, L, B):
+    w = custom(f"heads-H{H}-L{L}-B{B}", H, (L,), 128, B, 0.4, "bf16", seed=700 + H)
+    res = gpu_run(w, want_stats=True)
+    pairs = []
+    for h in range(H):
+        ref, out_ref, nsel = oracle_head(res, h)
+        check_stats(res, h, ref)
+        pairs.append(compare_rows(res, h, out_ref, range(len(ref["S"])), B))
+    assert_close(pairs, res["dtype"], f"ranges across heads H={H} L={L} B={B}")
