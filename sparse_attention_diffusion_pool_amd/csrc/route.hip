@@ -7,16 +7,72 @@
 // in fp32 with a fixed summation order (c = 0..d-1). Selection keeps the k largest scores, ties
 // to the smaller j, and writes S_i as ascending block indices.
 //
-// One workgroup = 4 waves = 16 query blocks of one head; wave w owns 4 rows. Key-block centroids
-// stream through LDS in tiles of 64 (lane = block within the tile) and are shared by the 16 rows.
-// Each lane keeps the scores of blocks j = 64 s + lane in registers as order-preserving uint32
-// keys; the k-th largest key is found MSB-first with wave ballots (32 rounds), then the blocks
-// are compacted in ascending j with ballot/popcount prefix sums.
+// One workgroup = 4 waves = 16 query blocks of one head (fewer for N_b > 1024); wave w selects
+// the rows 4w .. 4w + 3. d = 128 with 16 rows: the scores run on the fp32 matrix unit, each wave
+// taking 16 keys of every tile of 64 into registers straight from memory (one tile ahead), and
+// land as order-preserving uint32 keys in a per-workgroup LDS array; the waves meet once, then
+// select. Otherwise key-block centroids stream through LDS in tiles of 64 (lane = block within
+// the tile), shared by the rows, with fp32 FMA dot products, and every lane keeps its keys in
+// registers. The k-th largest key is found MSB-first with wave ballots, then the blocks are
+// compacted in ascending j with ballot/popcount prefix sums.
 #include "dev_common.h"
 #include "pisa_internal.h"
 
 namespace pisa {
 namespace {
+
+// RPW query blocks per wave (4 waves): fewer for large N_b so that the RPW x NS keys stay in
+// registers.
+// Radix select of one row's k largest keys and their compaction: lane l holds the keys of blocks
+// j = 64 s + l (0 for j >= N_b); writes the k selected j in ascending order to out.
+template <int NS>
+__device__ __forceinline__ void select_row(const uint32_t (&key)[NS], int Nb, int kk, int lane, int32_t* out) {
+  const uint64_t ltmask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // Every valid key lies between the row's smallest and largest, so all of them share the bits
+  // above the highest bit where those two differ: the k-th largest has them too, and the select
+  // starts below them (the same T as starting at bit 31, in fewer rounds).
+  uint32_t kmax = 0u, kmin = 0xffffffffu;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const bool valid = 64 * s + lane < Nb;
+    kmax = max(kmax, valid ? key[s] : 0u);
+    kmin = min(kmin, valid ? key[s] : 0xffffffffu);
+  }
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
+  }
+  kmax = __builtin_amdgcn_readfirstlane(kmax);
+  kmin = __builtin_amdgcn_readfirstlane(kmin);
+  const uint32_t diff = kmax ^ kmin;
+  const int top = diff ? 31 - __builtin_clz(diff) : -1;  // highest differing bit
+  // the shared prefix above `top` (all of kmax when every key is equal)
+  uint32_t T = top < 0 ? kmax : (top == 31 ? 0u : (kmax & ~((2u << top) - 1u)));
+  for (int b = top; b >= 0; --b) {
+    const uint32_t cand = T | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) cnt += __popcll(__ballot(key[s] >= cand));
+    if (cnt >= kk) T = cand;
+    // exactly k keys at or above cand: they are the k largest, whatever the lower bits decide
+    if (cnt == kk) break;
+  }
+  int gt = 0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) gt += __popcll(__ballot(key[s] > T));
+  const int need = kk - gt;
+  int eq_seen = 0, base = 0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const bool eq = key[s] == T;
+    const uint64_t eqm = __ballot(eq);
+    const bool take = key[s] > T || (eq && eq_seen + __popcll(eqm & ltmask) < need);
+    eq_seen += __popcll(eqm);
+    const uint64_t sm = __ballot(take);
+    if (take) out[base + __popcll(sm & ltmask)] = 64 * s + lane;
+    base += __popcll(sm);
+  }
+}
 
 // RPW query blocks per wave (4 waves): fewer for large N_b so that the RPW x NS keys stay in
 // registers.
@@ -28,36 +84,43 @@ __global__ __launch_bounds__(256) void route_kernel(Dims dm, Work w) {
   constexpr bool kMatrix = D == 128 && kRows == 16;
   constexpr int STR = D + 4;  // padded row stride (floats) of the LDS tiles
   __shared__ __attribute__((aligned(16))) float qs[kRows][STR];
-  __shared__ float qn[kRows];
   const int h = blockIdx.y, i0 = blockIdx.x * kRows;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int Nb = dm.Nb;
   const float* qbar = w.qbar + (size_t)h * Nb * D;
   const float* kbar = w.kbar + (size_t)h * Nb * D;
   const float* M = w.M + (size_t)h * Nb;
+  const int kk = dm.k;
 
+  {
+    // the workgroup's pooled queries, 16 bytes per load, all in flight at once; rows past N_b
+    // read as zeros (buffer range check)
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbar + (size_t)i0 * D, (uint32_t)max(0, Nb - i0) * D * 4);
+    constexpr int kAll = kRows * D / 4;                 // 16-byte pieces
+    constexpr int kPieces = (kAll + 255) / 256;         // per thread (the last round partial)
+    f32x4 qv[kPieces];
 #pragma unroll
-  for (int e = tid; e < kRows * D; e += 256) {  // all loads in flight at once
-    const int r = e / D, c = e % D;
-    qs[r][c] = (i0 + r < Nb) ? qbar[(size_t)(i0 + r) * D + c] : 0.f;
+    for (int it = 0; it < kPieces; ++it)
+      if (tid + 256 * it < kAll) qv[it] = __builtin_bit_cast(f32x4, buf_load16(rq, 16u * (tid + 256 * it)));
+#pragma unroll
+    for (int it = 0; it < kPieces; ++it) {
+      const int e = 4 * (tid + 256 * it);
+      if (tid + 256 * it < kAll) *reinterpret_cast<f32x4*>(&qs[e / D][e % D]) = qv[it];
+    }
   }
   __syncthreads();
-  if (tid < kRows) {
-    float s = 0.f;
-    for (int c = 0; c < D; ++c) s = fmaf(qs[tid][c], qs[tid][c], s);
-    qn[tid] = sqrtf(s);
-  }
 
-  // key[][] is indexed with compile-time indices only (every loop over it is unrolled), so that it
-  // stays in registers
-  uint32_t key[kRowsPerWave][NS];
   if constexpr (kMatrix) {
     // Scores on the fp32 matrix unit (v_mfma_f32_16x16x4_f32): rows = the workgroup's 16 query
     // blocks, columns = 16 keys per wave and tile of 64. The sum over d runs as 32 steps of 4
     // with lane l covering d = 32 (l / 16) + t at step t (A: row l % 16, B: key l % 16), so each
     // lane's operands are 32 consecutive floats of one row. Lane l then holds the scores of rows
-    // 4 (l / 16) .. + 3 for its key; they pass through LDS to the select layout (lane = key).
-    __shared__ float scl[16][65];
+    // 4 (l / 16) .. + 3 for its key. They go to the workgroup's score array as order-preserving
+    // keys (rows KS floats apart, KS = 4 mod 64: the 64 lanes' writes fall in distinct banks), and
+    // the waves run through their tiles without meeting; one barrier ends the pass, then each
+    // wave selects its rows from the array.
+    constexpr int KS = 64 * NS + 4;
+    __shared__ uint32_t sk[16][KS];
     float qa[32];
     {
       const float* qrow = &qs[lane & 15][32 * (lane >> 4)];
@@ -68,15 +131,33 @@ __global__ __launch_bounds__(256) void route_kernel(Dims dm, Work w) {
         for (int e = 0; e < 4; ++e) qa[4 * t4 + e] = v[e];
       }
     }
-    f32x4 kb[8], kpre[8];
-    float mpre = 0.f;
-    auto fetch = [&](int jt) __attribute__((always_inline)) {
-      const int jk = jt + 16 * wave + (lane & 15);
-      const float* src = kbar + (size_t)jk * D + 32 * (lane >> 4);
+    // ||qbar|| of the rows this lane's scores belong to, 4 (l / 16) + r, from the operands: each
+    // lane sums the squares of its 32 values (d ascending), then the four lane groups of a row
+    // are added (groups 0 + 1, 2 + 3, then the two pairs)
+    float qn[4];
+    {
+      float ss = 0.f;
 #pragma unroll
-      for (int t4 = 0; t4 < 8; ++t4)
-        kpre[t4] = jk < Nb ? *reinterpret_cast<const f32x4*>(src + 4 * t4) : f32x4{0.f, 0.f, 0.f, 0.f};
-      mpre = jk < Nb ? M[jk] : 0.f;
+      for (int t = 0; t < 32; ++t) ss = fmaf(qa[t], qa[t], ss);
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      const float nrm = sqrtf(ss);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) qn[r] = __shfl(nrm, 4 * (lane >> 4) + r);
+    }
+    // The centroids of tile s + 1 are loaded while tile s is used, through buffer resources that
+    // end at N_b: keys past it read as zeros, and every tile issues the same loads, so the wait
+    // before a tile's use counts only the younger tile's loads.
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbar, (uint32_t)Nb * D * 4);
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(M, (uint32_t)Nb * 4);
+    f32x4 kb[8], kpre[8];
+    float mpre;
+    auto fetch = [&](int jt) __attribute__((always_inline)) {
+      const uint32_t jk = jt + 16 * wave + (lane & 15);
+      const uint32_t off = jk * (D * 4) + 128u * (lane >> 4);
+#pragma unroll
+      for (int t4 = 0; t4 < 8; ++t4) kpre[t4] = __builtin_bit_cast(f32x4, buf_load16(rk, off + 16u * t4));
+      mpre = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rm, 4u * jk, 0, 0));
     };
     fetch(0);
 #pragma unroll
@@ -85,25 +166,41 @@ __global__ __launch_bounds__(256) void route_kernel(Dims dm, Work w) {
 #pragma unroll
       for (int t4 = 0; t4 < 8; ++t4) kb[t4] = kpre[t4];
       const float mj = mpre;
-      if (jt + 64 < Nb) fetch(jt + 64);
+      if (s + 1 < NS) fetch(jt + 64);
+      // keep the loads here: the scheduler would otherwise sink them to their use a tile later
+      __builtin_amdgcn_sched_barrier(0);
       f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < 32; ++t) c = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[t], kb[t >> 2][t & 3], c, 0, 0, 0);
       const int jk = jt + 16 * wave + (lane & 15);
       const float nj = (jk == Nb - 1) ? (float)dm.n_last : (float)dm.B;
-      __syncthreads();  // previous tile's scores read (and qn visible on the first pass)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float sc = c[r];
-        if (dm.routing == 0) sc += logf(fmaf(qn[4 * (lane >> 4) + r], mj, nj));
-        scl[4 * (lane >> 4) + r][16 * wave + (lane & 15)] = sc;
+        if (dm.routing == 0) sc += logf(fmaf(qn[r], mj, nj));
+        sk[4 * (lane >> 4) + r][jk] = jk < Nb ? float_order_key(sc) : 0u;
       }
-      __syncthreads();
-      const bool valid = jt + lane < Nb;
+    }
+    __syncthreads();
 #pragma unroll
-      for (int r = 0; r < kRowsPerWave; ++r) key[r][s] = valid ? float_order_key(scl[kRowsPerWave * wave + r][lane]) : 0u;
+    for (int r = 0; r < kRowsPerWave; ++r) {
+      const int i = i0 + kRowsPerWave * wave + r;
+      if (i >= Nb) break;  // uniform per wave
+      uint32_t key[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) key[s] = sk[kRowsPerWave * wave + r][64 * s + lane];
+      select_row<NS>(key, Nb, kk, lane, w.idx + ((size_t)h * Nb + i) * kk);
     }
   } else {
+    __shared__ float qn[kRows];
+    if (tid < kRows) {
+      float s2 = 0.f;
+      for (int c = 0; c < D; ++c) s2 = fmaf(qs[tid][c], qs[tid][c], s2);
+      qn[tid] = sqrtf(s2);
+    }
+    // key[][] is indexed with compile-time indices only (every loop over it is unrolled), so that
+    // it stays in registers
+    uint32_t key[kRowsPerWave][NS];
     __shared__ __attribute__((aligned(16))) float kt[64][STR];
     // The next centroid tile (this thread's share, and M_j of the lane's key) is loaded into
     // registers while the current one is used, so one tile's load latency overlaps the previous
@@ -164,58 +261,11 @@ __global__ __launch_bounds__(256) void route_kernel(Dims dm, Work w) {
         key[r][s] = valid ? float_order_key(sc) : 0u;
       }
     }
-  }
-
-  const uint64_t ltmask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int kk = dm.k;
 #pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r) {
-    const int i = i0 + kRowsPerWave * wave + r;
-    if (i >= Nb) break;  // uniform per wave
-    // Every valid key lies between the row's smallest and largest, so all of them share the bits
-    // above the highest bit where those two differ: the k-th largest has them too, and the
-    // select starts below them (the same T as starting at bit 31, in fewer rounds).
-    uint32_t kmax = 0u, kmin = 0xffffffffu;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const bool valid = 64 * s + lane < Nb;
-      kmax = max(kmax, valid ? key[r][s] : 0u);
-      kmin = min(kmin, valid ? key[r][s] : 0xffffffffu);
-    }
-    for (int o = 32; o >= 1; o >>= 1) {
-      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
-      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o));
-    }
-    kmax = __builtin_amdgcn_readfirstlane(kmax);
-    kmin = __builtin_amdgcn_readfirstlane(kmin);
-    const uint32_t diff = kmax ^ kmin;
-    const int top = diff ? 31 - __builtin_clz(diff) : -1;  // highest differing bit
-    // the shared prefix above `top` (all of kmax when every key is equal)
-    uint32_t T = top < 0 ? kmax : (top == 31 ? 0u : (kmax & ~((2u << top) - 1u)));
-    for (int b = top; b >= 0; --b) {
-      const uint32_t cand = T | (1u << b);
-      int cnt = 0;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) cnt += __popcll(__ballot(key[r][s] >= cand));
-      if (cnt >= kk) T = cand;
-      // exactly k keys at or above cand: they are the k largest, whatever the lower bits decide
-      if (cnt == kk) break;
-    }
-    int gt = 0;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) gt += __popcll(__ballot(key[r][s] > T));
-    const int need = kk - gt;
-    int eq_seen = 0, base = 0;
-    int32_t* out = w.idx + ((size_t)h * Nb + i) * kk;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const bool eq = key[r][s] == T;
-      const uint64_t eqm = __ballot(eq);
-      const bool take = key[r][s] > T || (eq && eq_seen + __popcll(eqm & ltmask) < need);
-      eq_seen += __popcll(eqm);
-      const uint64_t sm = __ballot(take);
-      if (take) out[base + __popcll(sm & ltmask)] = 64 * s + lane;
-      base += __popcll(sm);
+    for (int r = 0; r < kRowsPerWave; ++r) {
+      const int i = i0 + kRowsPerWave * wave + r;
+      if (i >= Nb) break;  // uniform per wave
+      select_row<NS>(key[r], Nb, kk, lane, w.idx + ((size_t)h * Nb + i) * kk);
     }
   }
 }
