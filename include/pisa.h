@@ -145,10 +145,10 @@ pisa_status pisa_forward(pisa_plan_t *plan, const void *Q, const void *K, const 
 
 /* pisa_forward without an attached workspace, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). The
- * statistics, selection and H-bar live in a static device array of 160 MiB per GPU (allocated
+ * statistics, selection and H-bar live in a static device array of 96 MiB per GPU (allocated
  * when the library's code is loaded, held until the process ends), which covers plans whose
- * workspace_bytes is at most 160 MiB (every bundled workload: the Wan2.1-14B-like 720p layer needs
- * 149 MiB); a larger plan gives PISA_ERR_WORKSPACE. The call allocates nothing and needs no
+ * workspace_bytes is at most 96 MiB (every bundled workload: the Wan2.1-14B-like 720p layer needs
+ * 91 MiB); a larger plan gives PISA_ERR_WORKSPACE. The call allocates nothing and needs no
  * attached workspace (one attached to the plan is ignored). Every call on a GPU shares that GPU's
  * array and leaves its contents behind (every part is written before it is read, so nothing needs
  * clearing): calls that can overlap on one GPU (two streams, two threads) race and must be

@@ -81,8 +81,8 @@ struct Layout {
 Layout workspace_layout(const Dims& dm);
 
 // Size of the static workspace of pisa_forward_noalloc (a file-scope device array per GPU): the
-// plans of every bundled workload fit (the Wan2.1-14B-like 720p layer needs 149 MiB).
-constexpr size_t kStaticWorkspaceBytes = size_t(160) << 20;
+// plans of every bundled workload fit (the largest, the Wan2.1-14B-like 720p layer, needs 91 MiB).
+constexpr size_t kStaticWorkspaceBytes = size_t(96) << 20;
 
 // Device address of that array on the stream's device (looked up once per device, then cached).
 hipError_t static_workspace(hipStream_t stream, void** ptr);
