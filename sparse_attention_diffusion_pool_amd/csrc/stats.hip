@@ -126,7 +126,8 @@ __global__ __launch_bounds__(256) void stats_qbar_bf16(Dims dm, Work w, const __
 //
 // The copies are issued from assembly (copy_tile_chunks), out of sight of the compiler's
 // wait-count insertion, which cannot tell copies into one slot from reads of the other and would
-// make every read wait for the latest copy. The loops issue no other global loads, so the waits
+// make every read wait for the latest copy. The loops issue no other global loads (the covariance
+// pass's H-bar rows, loaded when a range enters a head, are followed by a full wait), so the waits
 // below (for all but the copies of the half issued after the one needed) are the only ones.
 template <int BLK>
 __device__ __forceinline__ void kv_half_copy(const __bf16* K, const __bf16* V, size_t r0, int n, int half,
@@ -157,8 +158,9 @@ __device__ __forceinline__ void lds_barrier() {
   __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// s_waitcnt vmcnt(N), expcnt and lgkmcnt at their maxima (N < 16). Vector-memory operations
-// complete in issue order, so this waits for everything issued before the N most recent.
+// s_waitcnt vmcnt(N), expcnt and lgkmcnt at their maxima (N < 16). Vector-memory loads complete
+// in issue order: once at most N operations are outstanding, every load issued before the N most
+// recent operations has landed.
 template <int N>
 __device__ __forceinline__ void wait_vmem_but() {
   static_assert(N >= 0 && N < 16, "vmcnt immediate");
