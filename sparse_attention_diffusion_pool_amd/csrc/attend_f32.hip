@@ -2,9 +2,10 @@
 // Same three phases and the same online-softmax state as the bf16 kernel (gist.science summary
 // of the PISA paper, section 2 "Core algorithm" and "Hardware implementation").
 //
-// One workgroup per (head, query block); D/32 adjacent threads share a query row, each owning
-// 32 of its dimensions (q, accumulator). Scores are reduced across those threads with shuffles,
-// so every thread of a row holds the row's full softmax state (max m, sum l, beta).
+// One workgroup per (head, query block); 8 adjacent threads share a query row, each owning D/8
+// of its dimensions (q, accumulator), so that a key's dot product is a short chain per thread.
+// Scores are reduced across those threads with DPP lane moves, so every thread of a row holds the
+// row's full softmax state (max m, sum l, beta). Tiles move in 16-byte pieces.
 // Phase 2 keeps the pages' form: e = 2^{s log2e scale - m}, l += n_j e, beta += e, O += e sumV_j,
 // with the shift m covering s + log2 n_j.
 #include "dev_common.h"
@@ -15,19 +16,49 @@ namespace {
 
 constexpr int kMaskWords = (8192 + 128) / 32;
 
-template <int TPR>
-__device__ __forceinline__ float row_reduce(float x) {
-  x += __shfl_xor(x, 1);
-  if (TPR == 4) x += __shfl_xor(x, 2);
+// Sum over the 8 adjacent lanes (aligned) that share a row, on DPP lane moves: the neighbour in
+// the quad (quad_perm 1,0,3,2), the other pair of the quad (2,3,0,1), then the other quad of the
+// 8 lanes (row_half_mirror maps lane i to 7 - i). Every lane of the 8 ends with the same sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_reduce8(float x) {
+  x += dpp_move<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_move<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_move<0x141>(x);  // row_half_mirror
   return x;
 }
 
+// NA tiles of rows x D floats from global (row stride D) into LDS, 16 bytes per load, all of the
+// thread's loads in flight before the first store; rows >= valid read as 0
+template <int D, int ROWS, int NTH, int NA = 1>
+__device__ __forceinline__ void tiles_in(float* const (&dst)[NA], const float* const (&src)[NA], int valid, int tid) {
+  constexpr int kAll = ROWS * D / 4, kPer = (kAll + NTH - 1) / NTH;
+  f32x4 v[NA][kPer];
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e4 = tid + NTH * u;
+      const bool ok = e4 < kAll && (4 * e4) / D < valid;
+      v[a][u] = ok ? *reinterpret_cast<const f32x4*>(src[a] + 4 * e4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e4 = tid + NTH * u;
+      if (e4 < kAll) *reinterpret_cast<f32x4*>(dst[a] + 4 * e4) = v[a][u];
+    }
+}
+
 template <int D, int BLK>
-__global__ __launch_bounds__(BLK * (D / 32)) void attend_f32(Dims dm, Work w, const float* __restrict__ Q,
+__global__ __launch_bounds__(BLK * 8) void attend_f32(Dims dm, Work w, const float* __restrict__ Q,
                                                              const float* __restrict__ K,
                                                              const float* __restrict__ V,
                                                              float* __restrict__ out) {
-  constexpr int TPR = D / 32, NTH = BLK * TPR, CH = 16;
+  constexpr int TPR = 8, DPT = D / TPR, NTH = BLK * TPR, CH = 16;  // row_reduce8: TPR = 8
   constexpr int LDSF = (2 * BLK * D > D * D + BLK * D) ? 2 * BLK * D : D * D + BLK * D;
   __shared__ __attribute__((aligned(16))) float smem[LDSF];
   __shared__ uint32_t selm[kMaskWords];
@@ -40,13 +71,18 @@ __global__ __launch_bounds__(BLK * (D / 32)) void attend_f32(Dims dm, Work w, co
   const int Nb = dm.Nb, B = dm.B, kk = dm.k;
   const int n_i = (i == Nb - 1) ? dm.n_last : B;
   const size_t head = (size_t)h * dm.L * D;
-  const int c0 = 32 * sub;
+  const int c0 = DPT * sub;
 
-  float q[32], O[32];
-  for (int c = 0; c < 32; ++c) {
-    q[c] = row < n_i ? Q[head + (size_t)(i * B + row) * D + c0 + c] : 0.f;
-    O[c] = 0.f;
+  float q[DPT], O[DPT];
+#pragma unroll
+  for (int c4 = 0; c4 < DPT / 4; ++c4) {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (row < n_i) v = *reinterpret_cast<const f32x4*>(Q + head + (size_t)(i * B + row) * D + c0 + 4 * c4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[4 * c4 + e] = v[e];
   }
+#pragma unroll
+  for (int c = 0; c < DPT; ++c) O[c] = 0.f;
   const int nmask = (dm.Nbp + 31) / 32;
   for (int t = tid; t < nmask; t += NTH) selm[t] = 0u;
   __syncthreads();
@@ -57,25 +93,56 @@ __global__ __launch_bounds__(BLK * (D / 32)) void attend_f32(Dims dm, Work w, co
   float m = -INFINITY, l = 0.f, beta = 0.f;
 
   // ---- phase 1 ----
+  // The next block's K and V are loaded into registers (this thread's 16-byte pieces) while the
+  // current block is used, where the registers allow (up to 64 x 128 or 128 x 64 floats a tile).
+  constexpr int kPer = BLK * D / 4 / NTH;
+  constexpr bool kPrefetch = BLK * D <= 8192;
+  f32x4 pk[kPrefetch ? kPer : 1], pv[kPrefetch ? kPer : 1];
+  auto fetch = [&](int it) __attribute__((always_inline)) {
+    const int j = sel[it];
+    const int n_j = (j == Nb - 1) ? dm.n_last : B;
+    const float* kb = K + head + (size_t)j * B * D;
+    const float* vb = V + head + (size_t)j * B * D;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e4 = tid + NTH * u;
+      const bool ok = (4 * e4) / D < n_j;
+      pk[u] = ok ? *reinterpret_cast<const f32x4*>(kb + 4 * e4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      pv[u] = ok ? *reinterpret_cast<const f32x4*>(vb + 4 * e4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  if constexpr (kPrefetch) {
+    if (kk > 0) fetch(0);
+  }
   for (int it = 0; it < kk; ++it) {
     const int j = sel[it];
     const int n_j = (j == Nb - 1) ? dm.n_last : B;
     __syncthreads();
-    for (int e = tid; e < BLK * D; e += NTH) {
-      const int r = e / D;
-      const size_t g = head + (size_t)j * B * D + e;
-      Ks[e] = r < n_j ? K[g] : 0.f;
-      Vs[e] = r < n_j ? V[g] : 0.f;
+    if constexpr (kPrefetch) {
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int e4 = tid + NTH * u;
+        *reinterpret_cast<f32x4*>(Ks + 4 * e4) = pk[u];
+        *reinterpret_cast<f32x4*>(Vs + 4 * e4) = pv[u];
+      }
+    } else {
+      tiles_in<D, BLK, NTH, 2>({Ks, Vs}, {K + head + (size_t)j * B * D, V + head + (size_t)j * B * D}, n_j, tid);
     }
     __syncthreads();
+    if constexpr (kPrefetch) {
+      if (it + 1 < kk) fetch(it + 1);
+      // keep the loads here: the scheduler would otherwise sink them to their use a block later
+      __builtin_amdgcn_sched_barrier(0);
+    }
     for (int n0 = 0; n0 < BLK; n0 += CH) {
       float s[CH];
       float mx = -INFINITY;
 #pragma unroll 2
       for (int x = 0; x < CH; ++x) {
         float part = 0.f;
-        for (int c = 0; c < 32; ++c) part = fmaf(q[c], Ks[(n0 + x) * D + c0 + c], part);
-        const float full = row_reduce<TPR>(part);
+#pragma unroll
+        for (int c = 0; c < DPT; ++c) part = fmaf(q[c], Ks[(n0 + x) * D + c0 + c], part);
+        const float full = row_reduce8(part);
         s[x] = (n0 + x < n_j) ? full * cs : -INFINITY;
         mx = fmaxf(mx, s[x]);
       }
@@ -84,12 +151,14 @@ __global__ __launch_bounds__(BLK * (D / 32)) void attend_f32(Dims dm, Work w, co
       m = m_new;
       l *= alpha;
       beta *= alpha;
-      for (int c = 0; c < 32; ++c) O[c] *= alpha;
+#pragma unroll
+      for (int c = 0; c < DPT; ++c) O[c] *= alpha;
 #pragma unroll 2
       for (int x = 0; x < CH; ++x) {
         const float p = exp2f(s[x] - m);
         l += p;
-        for (int c = 0; c < 32; ++c) O[c] = fmaf(p, Vs[(n0 + x) * D + c0 + c], O[c]);
+#pragma unroll
+        for (int c = 0; c < DPT; ++c) O[c] = fmaf(p, Vs[(n0 + x) * D + c0 + c], O[c]);
       }
     }
   }
@@ -102,12 +171,7 @@ __global__ __launch_bounds__(BLK * (D / 32)) void attend_f32(Dims dm, Work w, co
     const float lgB = log2f((float)B), lgLast = log2f((float)dm.n_last);
     for (int cb = 0; cb < dm.Nbp; cb += BLK) {
       __syncthreads();
-      for (int e = tid; e < BLK * D; e += NTH) {
-        const int r = e / D;
-        const bool ok = cb + r < Nb;
-        Ks[e] = ok ? kb[(size_t)cb * D + e] : 0.f;
-        Vs[e] = ok ? vs[(size_t)cb * D + e] : 0.f;
-      }
+      tiles_in<D, BLK, NTH, 2>({Ks, Vs}, {kb + (size_t)cb * D, vs + (size_t)cb * D}, Nb - cb, tid);
       __syncthreads();
       for (int n0 = 0; n0 < BLK; n0 += CH) {
         float s[CH];
@@ -116,8 +180,9 @@ __global__ __launch_bounds__(BLK * (D / 32)) void attend_f32(Dims dm, Work w, co
         for (int x = 0; x < CH; ++x) {
           const int j = cb + n0 + x;
           float part = 0.f;
-          for (int c = 0; c < 32; ++c) part = fmaf(q[c], Ks[(n0 + x) * D + c0 + c], part);
-          const float full = row_reduce<TPR>(part);
+#pragma unroll
+          for (int c = 0; c < DPT; ++c) part = fmaf(q[c], Ks[(n0 + x) * D + c0 + c], part);
+          const float full = row_reduce8(part);
           const bool ok = j < Nb && !((selm[j >> 5] >> (j & 31)) & 1u);
           s[x] = ok ? full * cs : -INFINITY;
           mx = fmaxf(mx, s[x] + (j == Nb - 1 ? lgLast : lgB));
@@ -127,7 +192,8 @@ __global__ __launch_bounds__(BLK * (D / 32)) void attend_f32(Dims dm, Work w, co
         m = m_new;
         l *= alpha;
         beta *= alpha;
-        for (int c = 0; c < 32; ++c) O[c] *= alpha;
+#pragma unroll
+        for (int c = 0; c < DPT; ++c) O[c] *= alpha;
 #pragma unroll 2
         for (int x = 0; x < CH; ++x) {
           const int j = cb + n0 + x;
@@ -135,7 +201,8 @@ __global__ __launch_bounds__(BLK * (D / 32)) void attend_f32(Dims dm, Work w, co
           const float nj = (j == Nb - 1) ? (float)dm.n_last : (float)B;
           l = fmaf(e, nj, l);
           beta += e;
-          for (int c = 0; c < 32; ++c) O[c] = fmaf(e, Vs[(n0 + x) * D + c0 + c], O[c]);
+#pragma unroll
+          for (int c = 0; c < DPT; ++c) O[c] = fmaf(e, Vs[(n0 + x) * D + c0 + c], O[c]);
         }
       }
     }
@@ -147,13 +214,15 @@ __global__ __launch_bounds__(BLK * (D / 32)) void attend_f32(Dims dm, Work w, co
     float* Qs = smem + D * D;
     __syncthreads();
     const float* hb = w.hbar + (size_t)h * D * D;
-    for (int e = tid; e < D * D; e += NTH) Hs[e] = hb[e];
-    for (int c = 0; c < 32; ++c) Qs[row * D + c0 + c] = q[c];
+    tiles_in<D, D, NTH>({Hs}, {hb}, D, tid);
+#pragma unroll
+    for (int c = 0; c < DPT; ++c) Qs[row * D + c0 + c] = q[c];
     __syncthreads();
     const float bs = beta * dm.scale;
 #pragma unroll 1
-    for (int c = 0; c < 32; ++c) {
+    for (int c = 0; c < DPT; ++c) {
       float t = 0.f;
+#pragma unroll 8
       for (int a = 0; a < D; ++a) t = fmaf(Qs[row * D + a], Hs[a * D + c0 + c], t);
       O[c] = fmaf(bs, t, O[c]);
     }
@@ -162,7 +231,10 @@ __global__ __launch_bounds__(BLK * (D / 32)) void attend_f32(Dims dm, Work w, co
   if (row < n_i) {
     const float inv = 1.0f / l;
     float* o = out + head + (size_t)(i * B + row) * D + c0;
-    for (int c = 0; c < 32; ++c) o[c] = O[c] * inv;
+#pragma unroll
+    for (int c4 = 0; c4 < DPT / 4; ++c4)
+      *reinterpret_cast<f32x4*>(o + 4 * c4) =
+          f32x4{O[4 * c4] * inv, O[4 * c4 + 1] * inv, O[4 * c4 + 2] * inv, O[4 * c4 + 3] * inv};
   }
 }
 
@@ -176,7 +248,7 @@ hipError_t launch_attend_f32(const Dims& dm, const Work& w, const void* Q, const
   auto v = static_cast<const float*>(V);
   auto o = static_cast<float*>(out);
 #define PISA_F32(D, BLK) \
-  hipLaunchKernelGGL((attend_f32<D, BLK>), dim3(items), dim3(BLK * (D / 32)), 0, s, dm, w, q, k, v, o)
+  hipLaunchKernelGGL((attend_f32<D, BLK>), dim3(items), dim3(BLK * 8), 0, s, dm, w, q, k, v, o)
   if (dm.d == 64 && dm.B == 64) PISA_F32(64, 64);
   else if (dm.d == 64) PISA_F32(64, 128);
   else if (dm.B == 64) PISA_F32(128, 64);
