@@ -145,10 +145,10 @@ void derive(pisa::Dims& dm, double keep) {
   if (kk < 1) kk = 1;
   if (kk > dm.Nb) kk = dm.Nb;
   dm.k = (int)kk;
-  // statistics workgroups: chunks of 16 blocks, halved (down to 4) while there are fewer than
-  // 512 workgroups (two per CU), so that small layers still fill the chip
+  // fp32 statistics workgroups: chunks of 16 blocks, halved (down to 1) while there are fewer
+  // than 512 workgroups (two per CU), so that small layers still spread over the chip
   dm.chunk = pisa::kStatsChunk;
-  while (dm.chunk > 4 && (long long)((dm.Nb + dm.chunk - 1) / dm.chunk) * dm.H < 512) dm.chunk /= 2;
+  while (dm.chunk > 1 && (long long)((dm.Nb + dm.chunk - 1) / dm.chunk) * dm.H < 512) dm.chunk /= 2;
   dm.NC = (dm.Nb + dm.chunk - 1) / dm.chunk;
   // bf16 statistics passes: one range of (head, block) pairs per workgroup, two workgroups per CU
   // on a 256-CU chip, and at least about 4 blocks per range so that each partial sum written

@@ -646,6 +646,7 @@ __global__ __launch_bounds__(256) void stats_f32(Dims dm, Work w, const float* _
     if (!COV) __syncthreads();  // every thread done with the previous block's ckb / cvs
     if (!COV && tid < D) {
       float sq = 0.f, sk = 0.f, sv = 0.f;
+#pragma unroll 8
       for (int r = 0; r < n; ++r) {
         sq += Q[r0 + (size_t)r * D + tid];
         sk += K[r0 + (size_t)r * D + tid];
@@ -660,11 +661,26 @@ __global__ __launch_bounds__(256) void stats_f32(Dims dm, Work w, const float* _
     }
     for (int s0 = 0; s0 < n; s0 += SUB) {
       __syncthreads();
-      for (int e = tid; e < SUB * D; e += 256) {
-        const int r = e / D, cc = e % D;
-        const bool ok = s0 + r < n;
-        Ks[r][cc] = ok ? K[r0 + (size_t)(s0 + r) * D + cc] : 0.f;
-        Vs[r][cc] = ok ? V[r0 + (size_t)(s0 + r) * D + cc] : 0.f;
+      {  // 16-byte loads, all of the thread's in flight before the first store
+        constexpr int kPer = SUB * D / 4 / 256;
+        f32x4 kv4[kPer], vv4[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+          const int e = 4 * (tid + 256 * u), r = e / D, cc = e % D;
+          const bool ok = s0 + r < n;
+          const size_t g = r0 + (size_t)(s0 + r) * D + cc;
+          kv4[u] = ok ? *reinterpret_cast<const f32x4*>(K + g) : f32x4{0.f, 0.f, 0.f, 0.f};
+          vv4[u] = ok ? *reinterpret_cast<const f32x4*>(V + g) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+          const int e = 4 * (tid + 256 * u), r = e / D, cc = e % D;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            Ks[r][cc + x] = kv4[u][x];
+            Vs[r][cc + x] = vv4[u][x];
+          }
+        }
       }
       __syncthreads();
       for (int r = 0; r < SUB; ++r)
